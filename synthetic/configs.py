@@ -1,0 +1,261 @@
+"""Seeded generators for the layer shapes the GPTQ-2D pages talk about.
+
+The pages ("GPTQ-2D: Cubic-Time Two-Sided Adaptive Rounding", Abstract) quantize
+the linear layers of Llama-3.1-70B-Instruct under a Kronecker-factored Hessian.
+Neither the weights nor the calibration data exist here, so these seeded,
+synthetic layers stand in for them with 8B/70B-class projection shapes.
+
+Every array is produced in float64 with numpy's PCG64 generator and then rounded
+through the workload's native dtype, so the float32 and float64 runs of one
+workload solve exactly the same problem.  The recipes (seed, distributions,
+outliers, spectrum, damping) are documented next to each builder below.
+
+Only inputs are produced here: W (m x n), the SPD matrices A (m x m, acting on
+rows) and B (n x n, acting on columns), and the per-row grid scales
+``s_k = max_l |W_kl| / hi`` with hi = 2**(bits-1) - 1.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from typing import Callable, Dict, Optional
+
+import numpy as np
+
+CONFIG_NAMES = ("C1", "C2", "C3", "C4", "C4T", "C5")
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    W: np.ndarray        # (m, n) float64, values representable in `dtype`
+    A: np.ndarray        # (m, m) float64, symmetric
+    B: np.ndarray        # (n, n) float64, symmetric
+    scales: np.ndarray   # (m,) float64, representable in `dtype`
+    bits: int
+    dtype: str           # native dtype: "f32" or "f64"
+    recipe: str
+
+    @property
+    def m(self) -> int:
+        return self.W.shape[0]
+
+    @property
+    def n(self) -> int:
+        return self.W.shape[1]
+
+    @property
+    def lo(self) -> int:
+        return -(1 << (self.bits - 1))
+
+    @property
+    def hi(self) -> int:
+        return (1 << (self.bits - 1)) - 1
+
+    def cast(self, dtype: str):
+        """Return (W, A, B, scales) as contiguous arrays of `dtype` ("f32"/"f64")."""
+        np_dt = np.float32 if dtype == "f32" else np.float64
+        return tuple(np.ascontiguousarray(x, dtype=np_dt)
+                     for x in (self.W, self.A, self.B, self.scales))
+
+
+# --------------------------------------------------------------------------
+# building blocks (input generation only)
+# --------------------------------------------------------------------------
+
+def _round_through(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def _sym(x: np.ndarray) -> np.ndarray:
+    return 0.5 * (x + x.T)
+
+
+def _haar(rng: np.random.Generator, p: int) -> np.ndarray:
+    """Haar-random orthogonal matrix: QR of a Gaussian with the sign of diag(R) fixed."""
+    g = rng.standard_normal((p, p))
+    q, r = np.linalg.qr(g)
+    q *= np.sign(np.diag(r))[None, :]
+    return q
+
+
+def _spectral(rng: np.random.Generator, p: int, power: float, damp: float) -> np.ndarray:
+    """U diag(k^-power) U^T + damp * I with U Haar (config C2)."""
+    u = _haar(rng, p)
+    lam = np.arange(1, p + 1, dtype=np.float64) ** (-power)
+    return _sym((u * lam[None, :]) @ u.T) + damp * np.eye(p)
+
+
+def _wishart_ar1(rng: np.random.Generator, p: int, samples: int, rho: float) -> np.ndarray:
+    """X^T X / N from N samples of an AR(1) feature process, plus 1 % mean-diagonal damping."""
+    z = rng.standard_normal((samples, p))
+    x = np.empty_like(z)
+    x[:, 0] = z[:, 0]
+    c = np.sqrt(1.0 - rho * rho)
+    for j in range(1, p):
+        x[:, j] = rho * x[:, j - 1] + c * z[:, j]
+    a = _sym(x.T @ x) / samples
+    return a + 0.01 * np.mean(np.diag(a)) * np.eye(p)
+
+
+def _wishart_powerlaw(rng: np.random.Generator, p: int, samples: int, power: float) -> np.ndarray:
+    """X^T X / N with X = Z diag(sqrt(k^-power)) U^T (U Haar), plus 1 % damping."""
+    u = _haar(rng, p)
+    lam = np.arange(1, p + 1, dtype=np.float64) ** (-power)
+    z = rng.standard_normal((samples, p))
+    x = (z * np.sqrt(lam)[None, :]) @ u.T
+    del z, u
+    a = _sym(x.T @ x) / samples
+    return a + 0.01 * np.mean(np.diag(a)) * np.eye(p)
+
+
+def _wishart_iid(rng: np.random.Generator, p: int, samples: int, ridge: float) -> np.ndarray:
+    """X^T X / N + ridge * I with X i.i.d. N(0, 1) (config C1 and random small cases)."""
+    x = rng.standard_normal((samples, p))
+    return _sym(x.T @ x) / samples + ridge * np.eye(p)
+
+
+def _row_scales(w: np.ndarray, hi: int) -> np.ndarray:
+    return np.max(np.abs(w), axis=1) / float(hi)
+
+
+def _finish(name, w, a, b, bits, dtype, recipe) -> Workload:
+    w = _round_through(w, dtype)
+    a = _round_through(_sym(a), dtype)
+    b = _round_through(_sym(b), dtype)
+    hi = (1 << (bits - 1)) - 1
+    s = _round_through(_row_scales(w, hi), dtype)
+    return Workload(name, np.ascontiguousarray(w), np.ascontiguousarray(a),
+                    np.ascontiguousarray(b), np.ascontiguousarray(s), bits, dtype, recipe)
+
+
+def _streams(seed: int):
+    return [np.random.Generator(np.random.PCG64(s))
+            for s in np.random.SeedSequence(seed).spawn(4)]
+
+
+# --------------------------------------------------------------------------
+# the five layer recipes
+# --------------------------------------------------------------------------
+
+def _c1() -> Workload:
+    gw, ga, gb, _ = _streams(101)
+    w = 0.02 * gw.standard_normal((32, 32))
+    a = _wishart_iid(ga, 32, 256, 0.01)
+    b = _wishart_iid(gb, 32, 256, 0.01)
+    return _finish("C1", w, a, b, 4, "f64",
+                   "32x32 fp64; W~N(0,0.02^2); A,B = X^T X/256 + 0.01 I, X 256x32 N(0,1); 4-bit")
+
+
+def _c2() -> Workload:
+    gw, ga, gb, go = _streams(202)
+    m = n = 512
+    w = 0.02 * gw.standard_normal((m, n))
+    cols = go.choice(n, size=int(round(0.005 * n)), replace=False)
+    w[:, cols] *= 10.0
+    a = _spectral(ga, m, 1.5, 1e-3)
+    b = _spectral(gb, n, 1.5, 1e-3)
+    return _finish("C2", w, a, b, 4, "f32",
+                   "512x512 fp32; W~N(0,0.02^2), 3 outlier columns x10; "
+                   "A,B = U diag(k^-1.5) U^T + 1e-3 I (Haar U); 4-bit")
+
+
+def _c3() -> Workload:
+    gw, ga, gb, _ = _streams(303)
+    m = n = 4096
+    w = 0.015 * gw.standard_normal((m, n))
+    a = _wishart_ar1(ga, m, 2048, 0.3)
+    b = _wishart_ar1(gb, n, 2048, 0.3)
+    return _finish("C3", w, a, b, 4, "f32",
+                   "4096x4096 fp32; W~N(0,0.015^2); A,B Wishart of 2048 AR(1) samples rho=0.3 "
+                   "+ 1% mean-diagonal damping; 4-bit")
+
+
+def _c4() -> Workload:
+    gw, ga, gb, _ = _streams(404)
+    m, n = 14336, 4096
+    w = gw.standard_t(5.0, size=(m, n)) * (0.01 / np.sqrt(5.0 / 3.0))
+    a = _wishart_powerlaw(ga, m, 4096, 1.0)
+    b = _wishart_powerlaw(gb, n, 4096, 1.0)
+    return _finish("C4", w, a, b, 4, "f32",
+                   "14336x4096 fp32; W Student-t(5) std 0.01; A,B Wishart of 4096 samples with "
+                   "k^-1 spectrum (Haar U) + 1% damping; 4-bit")
+
+
+def _c4t() -> Workload:
+    base = make("C4")
+    w = np.ascontiguousarray(base.W.T)
+    return _finish("C4T", w, base.B, base.A, 4, "f32",
+                   "transpose of C4: W'=W^T, A'=B, B'=A, scales recomputed per row")
+
+
+def _c5() -> Workload:
+    gw, ga, gb, go = _streams(505)
+    m = n = 8192
+    w = 0.01 * gw.standard_normal((m, n))
+    k = int(round(0.001 * m * n))
+    idx = go.choice(m * n, size=k, replace=False)
+    w.reshape(-1)[idx] *= 20.0
+    a = _wishart_powerlaw(ga, m, 8192, 1.2)
+    b = _wishart_powerlaw(gb, n, 8192, 1.2)
+    return _finish("C5", w, a, b, 3, "f32",
+                   "8192x8192 fp32; W~N(0,0.01^2), 0.1% entries x20; A,B Wishart of 8192 samples "
+                   "with k^-1.2 spectrum (Haar U) + 1% damping; 3-bit")
+
+
+_BUILDERS: Dict[str, Callable[[], Workload]] = {
+    "C1": _c1, "C2": _c2, "C3": _c3, "C4": _c4, "C4T": _c4t, "C5": _c5,
+}
+
+SHAPES = {"C1": (32, 32, 4), "C2": (512, 512, 4), "C3": (4096, 4096, 4),
+          "C4": (14336, 4096, 4), "C4T": (4096, 14336, 4), "C5": (8192, 8192, 3)}
+
+
+def make(name: str, cache_dir: Optional[str] = None) -> Workload:
+    """Build workload `name` (deterministic).  With `cache_dir`, reuse an .npz cache."""
+    if name not in _BUILDERS:
+        raise KeyError(f"unknown workload {name!r}; known: {CONFIG_NAMES}")
+    path = None
+    if cache_dir:
+        os.makedirs(cache_dir, exist_ok=True)
+        path = os.path.join(cache_dir, f"workload_{name}.npz")
+        if os.path.exists(path):
+            z = np.load(path)
+            return Workload(name, z["W"], z["A"], z["B"], z["scales"], int(z["bits"]),
+                            str(z["dtype"]), str(z["recipe"]))
+    wl = _BUILDERS[name]()
+    if path:
+        tmp = path + ".tmp.npz"
+        np.savez(tmp, W=wl.W, A=wl.A, B=wl.B, scales=wl.scales, bits=wl.bits,
+                 dtype=wl.dtype, recipe=wl.recipe)
+        os.replace(tmp, path)
+    return wl
+
+
+def make_random(m: int, n: int, bits: int = 4, seed: int = 0, dtype: str = "f64",
+                kind: str = "wishart", samples: Optional[int] = None,
+                global_scale: bool = False) -> Workload:
+    """Small random problem for parity and pin tests.
+
+    kind = "wishart": A, B = X^T X / N + 0.05 I with N = max(p, 8) samples, which gives
+    dense, strongly coupled metrics (every feedback term matters);
+    kind = "identity_a" / "identity_b" / "diagonal": A and/or B replaced by the identity
+    or a random positive diagonal (reductions to one-sided GPTQ and to RTN).
+    global_scale=True uses one scale for all rows (needed by the transpose symmetry).
+    """
+    gw, ga, gb, _ = _streams(10_000 + seed)
+    w = 0.02 * gw.standard_normal((m, n))
+    na = samples or max(m, 8)
+    nb = samples or max(n, 8)
+    a = _wishart_iid(ga, m, na, 0.05)
+    b = _wishart_iid(gb, n, nb, 0.05)
+    if kind in ("identity_a", "diagonal"):
+        a = np.eye(m) if kind == "identity_a" else np.diag(ga.uniform(0.5, 2.0, m))
+    if kind in ("identity_b", "diagonal"):
+        b = np.eye(n) if kind == "identity_b" else np.diag(gb.uniform(0.5, 2.0, n))
+    wl = _finish(f"rand{m}x{n}b{bits}s{seed}{kind}", w, a, b, bits, dtype, f"random {kind}")
+    if global_scale:
+        wl.scales[:] = _round_through(np.array([np.max(np.abs(wl.W)) / wl.hi]), dtype)[0]
+    return wl
