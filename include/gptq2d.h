@@ -1,0 +1,117 @@
+/*
+ * gptq2d.h -- C ABI of the GPTQ-2D two-sided adaptive rounding library (gfx950).
+ *
+ * Operation (sources cited by page title and section):
+ *   "GPTQ-2D: Cubic-Time Two-Sided Adaptive Rounding" (arxivlens page), Abstract,
+ *   Results, Methodology, Technical contributions; mind-verse.de article "Neue
+ *   Ansaetze zur Effizienzsteigerung von Large Language Models durch GPTQ-2D",
+ *   sections "GPTQ-2D: Eine Weiterentwicklung der adaptiven Rundung" and "Die
+ *   algorithmische Neuerung und ihre Auswirkungen".
+ *
+ *   Given a real m x n matrix W, SPD matrices A (m x m, acting on rows) and
+ *   B (n x n, acting on columns) and per-row scales s, produce integer codes
+ *   Z in [lo, hi] = [-2^(bits-1), 2^(bits-1)-1] and Q = diag(s) Z by adaptive
+ *   rounding under tr(A (W-Q) B (W-Q)^T): the exact trajectory of one-dimensional
+ *   GPTQ on the row-major vectorisation of W with Gram A (x) B, computed in cubic
+ *   work by rounding anti-diagonals of W in parallel with separable rank-one
+ *   feedback.  The triangular feedback factors are U' = diag(U)^-1 U with
+ *   A^-1 = U^T U (U upper), i.e. GPTQ's inverse-Hessian Cholesky factor scaled to
+ *   a unit diagonal; rint is round-half-to-even of t/s followed by the clamp.
+ *
+ * Conventions for every entry point
+ *   - Matrices are dense, row-major and contiguous, in DEVICE memory.
+ *   - dtype selects the element type of all floating-point arguments of a call:
+ *     GPTQ2D_F32 (float) or GPTQ2D_F64 (double).  Factorisations always run in
+ *     float64 internally; in F32 mode the sweep runs in float32.
+ *   - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     null stream) and the call returns without synchronising.  The caller owns
+ *     every buffer; the library keeps no pointer after a call returns.
+ *   - Inputs are never modified.
+ *   - Return value: 0 on success; -i when argument i (1-based) is invalid, checked
+ *     on the host before any HIP call; a positive GPTQ2D_ERR_* code when a HIP
+ *     runtime call fails.  Numerical failures are reported through `info`, a
+ *     DEVICE int[2] that the call first clears (may be NULL): info[0] = 1 if A is
+ *     not positive definite, 2 if B is not, 3 if a scale is <= 0 or not finite;
+ *     info[1] = 1-based index of the failing pivot or row.  When info[0] != 0 the
+ *     outputs are undefined.
+ *   - workspace: DEVICE scratch of at least the size returned by the matching
+ *     *_workspace_bytes function, 256-byte aligned.  Passing NULL and 0 makes the
+ *     library allocate (and free) it stream-ordered on `stream`.
+ *   - Calls that overlap in time must not share a workspace.
+ */
+#ifndef GPTQ2D_H
+#define GPTQ2D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPTQ2D_F32 0
+#define GPTQ2D_F64 1
+
+#define GPTQ2D_ERR_HIP 1          /* a HIP runtime call failed */
+#define GPTQ2D_ERR_ALLOC 2        /* device allocation failed */
+
+/*
+ * Factor stage: the unit upper triangular feedback factor of one SPD matrix.
+ * (mind-verse article, "GPTQ-2D: Eine Weiterentwicklung der adaptiven Rundung":
+ * errors propagate through a triangular feedback matrix; arxivlens page,
+ * Limitations: fixed bases, factorisations computed once.)
+ *   p        order of A (>= 1)                                         [arg 1]
+ *   dtype    GPTQ2D_F32 or GPTQ2D_F64                                   [arg 2]
+ *   A        p x p SPD, symmetric; only the lower triangle is read      [arg 3]
+ *   U_unit   p x p output: U' (unit diagonal, upper; lower part zero)   [arg 4]
+ *   workspace, workspace_bytes  see conventions                      [args 5, 6]
+ *   info     device int[2] or NULL; info[0] = 1 if A is not SPD        [arg 7]
+ *   stream   hipStream_t                                                [arg 8]
+ */
+int gptq2d_factor(int64_t p, int dtype, const void* A, void* U_unit,
+                  void* workspace, size_t workspace_bytes, int* info, void* stream);
+size_t gptq2d_factor_workspace_bytes(int64_t p, int dtype);
+
+/*
+ * Sweep stage: two-sided adaptive rounding given both unit factors.
+ * (arxivlens page, Results/Methodology: anti-diagonal rounds in parallel with an
+ * accumulated-feedback buffer and rank-one separable updates.)
+ *   m, n     shape of W (>= 1 each)                                  [args 1, 2]
+ *   bits     grid width, 2..8                                           [arg 3]
+ *   dtype    GPTQ2D_F32 or GPTQ2D_F64                                   [arg 4]
+ *   W        m x n weights                                              [arg 5]
+ *   Ua_unit  m x m unit upper factor of A (as from gptq2d_factor)       [arg 6]
+ *   Ub_unit  n x n unit upper factor of B                               [arg 7]
+ *   scales   m per-row scales, > 0 and finite                           [arg 8]
+ *   codes    m x n int8 output, values in [lo, hi]                      [arg 9]
+ *   Q        m x n output, Q[k,l] = scales[k] * codes[k,l]             [arg 10]
+ *   workspace, workspace_bytes                                     [args 11, 12]
+ *   info     device int[2] or NULL; info[0] = 3 for a bad scale        [arg 13]
+ *   stream                                                             [arg 14]
+ */
+int gptq2d_quantize_factored(int64_t m, int64_t n, int bits, int dtype, const void* W,
+                             const void* Ua_unit, const void* Ub_unit, const void* scales,
+                             int8_t* codes, void* Q, void* workspace, size_t workspace_bytes,
+                             int* info, void* stream);
+size_t gptq2d_sweep_workspace_bytes(int64_t m, int64_t n, int dtype);
+
+/*
+ * Whole call: factor A and B, then sweep (the problem statement of both pages).
+ *   m, n, bits, dtype, W                                             [args 1-5]
+ *   A        m x m SPD (lower triangle read)                            [arg 6]
+ *   B        n x n SPD (lower triangle read)                            [arg 7]
+ *   scales, codes, Q, workspace, workspace_bytes, info, stream     [args 8-14]
+ */
+int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, const void* A,
+                    const void* B, const void* scales, int8_t* codes, void* Q,
+                    void* workspace, size_t workspace_bytes, int* info, void* stream);
+size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype);
+
+/* Static description of a return code (never NULL). */
+const char* gptq2d_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ2D_H */

@@ -1,0 +1,77 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments
+on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gptq2d.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import two_sided_adaptive_amd as g2d
+    if not os.path.exists(g2d.LIB_PATH):
+        from two_sided_adaptive_amd import build
+        build.build()
+    return g2d.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(gptq2d_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("gptq2d_quantize", "gptq2d_factor", "gptq2d_quantize_factored",
+                 "gptq2d_workspace_bytes", "gptq2d_strerror"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(os.path.join(ROOT, "two_sided_adaptive_amd", "libgptq2d.so"))
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_invalid_arguments_rejected_on_host(lib):
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    # m <= 0 -> -1, n <= 0 -> -2, bits -> -3, dtype -> -4, null W -> -5 ...
+    assert lib.gptq2d_quantize(0, 4, 4, 0, p, p, p, p, p, p, None, 0, None, None) == -1
+    assert lib.gptq2d_quantize(4, 0, 4, 0, p, p, p, p, p, p, None, 0, None, None) == -2
+    assert lib.gptq2d_quantize(4, 4, 1, 0, p, p, p, p, p, p, None, 0, None, None) == -3
+    assert lib.gptq2d_quantize(4, 4, 9, 0, p, p, p, p, p, p, None, 0, None, None) == -3
+    assert lib.gptq2d_quantize(4, 4, 4, 7, p, p, p, p, p, p, None, 0, None, None) == -4
+    assert lib.gptq2d_quantize(4, 4, 4, 0, None, p, p, p, p, p, None, 0, None, None) == -5
+    assert lib.gptq2d_quantize(4, 4, 4, 0, p, None, p, p, p, p, None, 0, None, None) == -6
+    assert lib.gptq2d_quantize(4, 4, 4, 0, p, p, None, p, p, p, None, 0, None, None) == -7
+    assert lib.gptq2d_quantize(4, 4, 4, 0, p, p, p, None, p, p, None, 0, None, None) == -8
+    assert lib.gptq2d_quantize(4, 4, 4, 0, p, p, p, p, None, p, None, 0, None, None) == -9
+    assert lib.gptq2d_quantize(4, 4, 4, 0, p, p, p, p, p, None, None, 0, None, None) == -10
+    assert lib.gptq2d_quantize(4, 4, 4, 0, p, p, p, p, p, p, p, 8, None, None) == -12
+    assert lib.gptq2d_quantize(4, 4, 4, 0, p, p, p, p, p, p, None, 8, None, None) == -12
+    assert lib.gptq2d_quantize_factored(4, 4, 4, 1, p, p, None, p, p, p, None, 0, None,
+                                        None) == -7
+    assert lib.gptq2d_factor(-3, 0, p, p, None, 0, None, None) == -1
+    assert lib.gptq2d_factor(8, 2, p, p, None, 0, None, None) == -2
+    assert lib.gptq2d_factor(8, 0, None, p, None, 0, None, None) == -3
+    assert lib.gptq2d_factor(8, 0, p, None, None, 0, None, None) == -4
+    assert lib.gptq2d_factor(8, 0, p, p, p, 16, None, None) == -6
+
+
+def test_workspace_sizes(lib):
+    assert lib.gptq2d_workspace_bytes(0, 3, 0) == 0
+    assert lib.gptq2d_workspace_bytes(3, 3, 5) == 0
+    small = lib.gptq2d_workspace_bytes(32, 32, 1)
+    assert small > 0 and small % 256 == 0
+    assert lib.gptq2d_sweep_workspace_bytes(4096, 4096, 0) >= 4 * 4096 * 4096 * 4
+    assert lib.gptq2d_workspace_bytes(4096, 4096, 1) > lib.gptq2d_workspace_bytes(4096, 4096, 0)
+
+
+def test_strerror(lib):
+    assert lib.gptq2d_strerror(0) == b"success"
+    assert b"argument" in lib.gptq2d_strerror(-3)
+    assert lib.gptq2d_strerror(12345)

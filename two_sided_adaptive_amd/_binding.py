@@ -1,0 +1,171 @@
+"""ctypes binding of libgptq2d.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; torch provides the
+device memory (outputs, workspace, info flags) and the current stream.  The names
+follow the C ABI in include/gptq2d.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgptq2d.so")
+F32, F64 = 0, 1
+_lib = None
+
+_SYMBOLS = {
+    "gptq2d_factor": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p, ctypes.c_void_p]),
+    "gptq2d_factor_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int]),
+    "gptq2d_quantize_factored": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                ctypes.c_int] + [ctypes.c_void_p] * 6 +
+                                 [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                  ctypes.c_void_p]),
+    "gptq2d_sweep_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64,
+                                                       ctypes.c_int]),
+    "gptq2d_quantize": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int] + [ctypes.c_void_p] * 6 +
+                        [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "gptq2d_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
+    "gptq2d_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+class GPTQ2DError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgptq2d.so; raise if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m "
+                          "two_sided_adaptive_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SYMBOLS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float64:
+        return F64
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or float64)")
+
+
+def _check_dev(name: str, t: torch.Tensor, dtype, shape) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raise_rc(rc: int, fn: str) -> None:
+    if rc != 0:
+        msg = load_library().gptq2d_strerror(rc).decode()
+        raise GPTQ2DError(f"{fn} returned {rc}: {msg}")
+
+
+_INFO_MSG = {1: "A is not positive definite (pivot {})", 2: "B is not positive definite (pivot {})",
+             3: "scale of row {} is not positive and finite"}
+
+
+def _check_info(info: torch.Tensor) -> None:
+    v = info.cpu().tolist()
+    if v[0] != 0:
+        raise GPTQ2DError(_INFO_MSG.get(v[0], "numerical failure {}").format(v[1]))
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def workspace_bytes(m: int, n: int, dtype: torch.dtype) -> int:
+    return load_library().gptq2d_workspace_bytes(m, n, F32 if dtype == torch.float32 else F64)
+
+
+def factor(A: torch.Tensor, check: bool = True) -> torch.Tensor:
+    """U' (unit upper) with A^-1 = U^T U, computed on the device (gptq2d_factor)."""
+    lib = load_library()
+    p = A.shape[0]
+    dt = _dt(A)
+    _check_dev("A", A, A.dtype, (p, p))
+    U = torch.empty_like(A)
+    ws = torch.empty(lib.gptq2d_factor_workspace_bytes(p, dt), dtype=torch.uint8, device=A.device)
+    info = torch.zeros(2, dtype=torch.int32, device=A.device)
+    rc = lib.gptq2d_factor(p, dt, A.data_ptr(), U.data_ptr(), ws.data_ptr(), ws.numel(),
+                           info.data_ptr(), _stream(A.device))
+    _raise_rc(rc, "gptq2d_factor")
+    if check:
+        _check_info(info)
+    return U
+
+
+def quantize_factored(W: torch.Tensor, Ua: torch.Tensor, Ub: torch.Tensor, bits: int,
+                      scales: torch.Tensor, check: bool = True,
+                      workspace: Optional[torch.Tensor] = None,
+                      out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Sweep only, given both unit factors (gptq2d_quantize_factored) -> (codes, Q)."""
+    lib = load_library()
+    m, n = W.shape
+    dt = _dt(W)
+    _check_dev("W", W, W.dtype, (m, n))
+    _check_dev("Ua", Ua, W.dtype, (m, m))
+    _check_dev("Ub", Ub, W.dtype, (n, n))
+    _check_dev("scales", scales, W.dtype, (m,))
+    codes, Q = out if out is not None else (
+        torch.empty((m, n), dtype=torch.int8, device=W.device), torch.empty_like(W))
+    need = lib.gptq2d_sweep_workspace_bytes(m, n, dt)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8,
+                                                             device=W.device)
+    info = torch.zeros(2, dtype=torch.int32, device=W.device)
+    rc = lib.gptq2d_quantize_factored(m, n, int(bits), dt, W.data_ptr(), Ua.data_ptr(),
+                                      Ub.data_ptr(), scales.data_ptr(), codes.data_ptr(),
+                                      Q.data_ptr(), ws.data_ptr(), ws.numel(), info.data_ptr(),
+                                      _stream(W.device))
+    _raise_rc(rc, "gptq2d_quantize_factored")
+    if check:
+        _check_info(info)
+    return codes, Q
+
+
+def quantize(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, bits: int, scales: torch.Tensor,
+             check: bool = True, workspace: Optional[torch.Tensor] = None,
+             out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Whole call: factor A and B, then sweep (gptq2d_quantize) -> (codes int8, Q)."""
+    lib = load_library()
+    m, n = W.shape
+    dt = _dt(W)
+    _check_dev("W", W, W.dtype, (m, n))
+    _check_dev("A", A, W.dtype, (m, m))
+    _check_dev("B", B, W.dtype, (n, n))
+    _check_dev("scales", scales, W.dtype, (m,))
+    codes, Q = out if out is not None else (
+        torch.empty((m, n), dtype=torch.int8, device=W.device), torch.empty_like(W))
+    need = lib.gptq2d_workspace_bytes(m, n, dt)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8,
+                                                             device=W.device)
+    info = torch.zeros(2, dtype=torch.int32, device=W.device)
+    rc = lib.gptq2d_quantize(m, n, int(bits), dt, W.data_ptr(), A.data_ptr(), B.data_ptr(),
+                             scales.data_ptr(), codes.data_ptr(), Q.data_ptr(), ws.data_ptr(),
+                             ws.numel(), info.data_ptr(), _stream(W.device))
+    _raise_rc(rc, "gptq2d_quantize")
+    if check:
+        _check_info(info)
+    return codes, Q

@@ -1,0 +1,24 @@
+// Internal host-side interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace g2d {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Factor stage (factor.hip): U' (dtype) of one SPD matrix A (dtype), fp64 inside.
+size_t factor_workspace(int64_t p);
+hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws, int* info,
+                          int side_code, hipStream_t s);
+
+// Sweep stage (sweep.hip): codes/Q from W, U'_a, U'_b, scales (all dtype).
+size_t sweep_workspace(int64_t m, int64_t n, int dtype);
+hipError_t sweep_enqueue(int64_t m, int64_t n, int bits, int dtype, const void* W,
+                         const void* Ua, const void* Ub, const void* scales, int8_t* codes,
+                         void* Q, void* ws, int* info, hipStream_t s);
+
+}  // namespace g2d
