@@ -107,6 +107,23 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
                     void* workspace, size_t workspace_bytes, int* info, void* stream);
 size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype);
 
+/*
+ * Measurement hook (not part of the method): when enabled, every kernel launch of
+ * the library is bracketed by a pair of HIP events on its stream and accounted to a
+ * kernel class (0 round, 1 near band, 2 potrf, 3 panel, 4 trailing, 5 trtri, 6 other,
+ * 7 far band)
+ * together with the algorithmic flops and HBM bytes of that launch.  Process-wide,
+ * off by default; it adds event records to the stream while on.
+ * gptq2d_profile_read waits for the recorded events, writes per-class totals since
+ * the previous read (milliseconds, launches, flops, bytes; host arrays, any pointer
+ * may be NULL) for the first min(n_classes, 8) classes and resets the totals.
+ * Returns 0, -1 if n_classes < 0, or GPTQ2D_ERR_HIP if an event query failed.
+ */
+int gptq2d_profile_enable(int on);
+int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* flops,
+                        double* bytes);
+const char* gptq2d_profile_class_name(int cls);
+
 /* Static description of a return code (never NULL). */
 const char* gptq2d_strerror(int status);
 

@@ -10,6 +10,8 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     factor,
     load_library,
+    profile_enable,
+    profile_read,
     quantize,
     quantize_factored,
     workspace_bytes,

@@ -33,6 +33,10 @@ _SYMBOLS = {
                         [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "gptq2d_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
     "gptq2d_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "gptq2d_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "gptq2d_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]),
+    "gptq2d_profile_class_name": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
 
@@ -169,3 +173,24 @@ def quantize(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, bits: int, scale
     if check:
         _check_info(info)
     return codes, Q
+
+
+def profile_enable(on: bool = True) -> None:
+    """Turn the library's per-kernel event timing on or off (gptq2d_profile_enable)."""
+    load_library().gptq2d_profile_enable(1 if on else 0)
+
+
+def profile_read() -> dict:
+    """Per-class totals since the last read: {name: (ms, launches, flops, bytes)}."""
+    import numpy as np
+    lib = load_library()
+    n = 8
+    ms = np.zeros(n)
+    la = np.zeros(n, dtype=np.int64)
+    fl = np.zeros(n)
+    by = np.zeros(n)
+    rc = lib.gptq2d_profile_read(n, ms.ctypes.data, la.ctypes.data, fl.ctypes.data,
+                                 by.ctypes.data)
+    _raise_rc(rc, "gptq2d_profile_read")
+    return {lib.gptq2d_profile_class_name(c).decode(): (float(ms[c]), int(la[c]), float(fl[c]),
+                                                         float(by[c])) for c in range(n)}

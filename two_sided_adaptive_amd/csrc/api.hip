@@ -2,10 +2,115 @@
 // host, workspace carve-up, and the factor -> sweep call sequence on one stream.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <vector>
+
 #include "../../include/gptq2d.h"
 #include "launch.hpp"
+#include "prof.hpp"
 
 using g2d::align_up;
+
+// ---------------------------------------------------------------------------
+// measurement hook (see prof.hpp)
+// ---------------------------------------------------------------------------
+namespace g2d {
+namespace {
+
+struct Pending {
+  int cls;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+
+struct ProfState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<Pending> pending;
+  hipEvent_t open[KC_COUNT] = {};
+  double ms[KC_COUNT] = {}, flops[KC_COUNT] = {}, bytes[KC_COUNT] = {};
+  int64_t launches[KC_COUNT] = {};
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    (void)hipEventCreate(&e);
+    return e;
+  }
+};
+
+ProfState& prof() {
+  static ProfState st;
+  return st;
+}
+
+}  // namespace
+
+bool prof_on() { return prof().on; }
+
+void prof_begin(int cls, hipStream_t s) {
+  ProfState& p = prof();
+  if (!p.on) return;
+  std::lock_guard<std::mutex> g(p.mu);
+  hipEvent_t e = p.get();
+  (void)hipEventRecord(e, s);
+  p.open[cls] = e;
+}
+
+void prof_end(int cls, hipStream_t s, double flops, double bytes) {
+  ProfState& p = prof();
+  if (!p.on) return;
+  std::lock_guard<std::mutex> g(p.mu);
+  hipEvent_t e = p.get();
+  (void)hipEventRecord(e, s);
+  p.pending.push_back(Pending{cls, p.open[cls], e, flops, bytes});
+  p.open[cls] = nullptr;
+}
+
+// per-device second stream and event pool
+namespace {
+struct DeviceRes {
+  hipStream_t aux = nullptr;
+  std::vector<hipEvent_t> events;
+};
+std::vector<DeviceRes>& device_res() {
+  static std::vector<DeviceRes> v;
+  return v;
+}
+}  // namespace
+
+std::recursive_mutex& lib_mutex() {
+  static std::recursive_mutex mu;
+  return mu;
+}
+
+hipError_t aux_resources(size_t nevents, hipStream_t* aux, hipEvent_t** events) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::vector<DeviceRes>& all = device_res();
+  if ((int)all.size() <= dev) all.resize(dev + 1);
+  DeviceRes& r = all[dev];
+  if (r.aux == nullptr) {
+    e = hipStreamCreateWithFlags(&r.aux, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+  }
+  while (r.events.size() < nevents) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    r.events.push_back(ev);
+  }
+  *aux = r.aux;
+  *events = r.events.data();
+  return hipSuccess;
+}
+
+}  // namespace g2d
 
 namespace {
 
@@ -115,7 +220,7 @@ size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype) {
   const size_t es = dtype == GPTQ2D_F32 ? sizeof(float) : sizeof(double);
   const size_t fa = g2d::factor_workspace(m), fb = g2d::factor_workspace(n);
   const size_t sw = g2d::sweep_workspace(m, n, dtype);
-  size_t scratch = fa > fb ? fa : fb;
+  size_t scratch = fa + fb;  // the two factorisations run concurrently
   if (sw > scratch) scratch = sw;
   return align_up((size_t)m * m * es) + align_up((size_t)n * n * es) + scratch;
 }
@@ -148,11 +253,67 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
   void* Ub = c;
   c += align_up((size_t)n * n * es);
   void* scratch = c;
-  hipError_t e = g2d::factor_enqueue(m, dtype, A, Ua, scratch, info, 1, s);
-  if (e == hipSuccess) e = g2d::factor_enqueue(n, dtype, B, Ub, scratch, info, 2, s);
+  void* scratch_b = c + g2d::factor_workspace(m);
+  // A's factor on the caller's stream, B's on the library's second stream; the sweep
+  // waits for both.
+  std::lock_guard<std::recursive_mutex> lock(g2d::lib_mutex());
+  hipStream_t s1 = nullptr;
+  hipEvent_t* ev = nullptr;
+  hipError_t e = g2d::aux_resources(2, &s1, &ev);
+  if (e == hipSuccess) e = hipEventRecord(ev[0], s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s1, ev[0], 0);
+  if (e == hipSuccess) e = g2d::factor_enqueue(m, dtype, A, Ua, scratch, info, 1, s);
+  if (e == hipSuccess) e = g2d::factor_enqueue(n, dtype, B, Ub, scratch_b, info, 2, s1);
+  if (e == hipSuccess) e = hipEventRecord(ev[1], s1);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s, ev[1], 0);
   if (e == hipSuccess)
     e = g2d::sweep_enqueue(m, n, bits, dtype, W, Ua, Ub, scales, codes, Q, scratch, info, s);
   return status(e);
+}
+
+int gptq2d_profile_enable(int on) {
+  g2d::ProfState& p = g2d::prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.on = on != 0;
+  return 0;
+}
+
+int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* flops,
+                        double* bytes) {
+  if (n_classes < 0) return -1;
+  g2d::ProfState& p = g2d::prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  int rc = 0;
+  for (const g2d::Pending& e : p.pending) {
+    float t = 0.f;
+    if (hipEventSynchronize(e.b) != hipSuccess || hipEventElapsedTime(&t, e.a, e.b) != hipSuccess)
+      rc = GPTQ2D_ERR_HIP;
+    p.ms[e.cls] += t;
+    p.flops[e.cls] += e.flops;
+    p.bytes[e.cls] += e.bytes;
+    p.launches[e.cls] += 1;
+    p.pool.push_back(e.a);
+    p.pool.push_back(e.b);
+  }
+  p.pending.clear();
+  const int n = n_classes < g2d::KC_COUNT ? n_classes : g2d::KC_COUNT;
+  for (int c = 0; c < n; ++c) {
+    if (ms) ms[c] = p.ms[c];
+    if (launches) launches[c] = p.launches[c];
+    if (flops) flops[c] = p.flops[c];
+    if (bytes) bytes[c] = p.bytes[c];
+  }
+  for (int c = 0; c < g2d::KC_COUNT; ++c) {
+    p.ms[c] = p.flops[c] = p.bytes[c] = 0.0;
+    p.launches[c] = 0;
+  }
+  return rc;
+}
+
+const char* gptq2d_profile_class_name(int cls) {
+  static const char* names[g2d::KC_COUNT] = {"round", "near", "potrf", "panel",
+                                             "trailing", "trtri", "other", "far"};
+  return (cls >= 0 && cls < g2d::KC_COUNT) ? names[cls] : "unknown";
 }
 
 const char* gptq2d_strerror(int st) {

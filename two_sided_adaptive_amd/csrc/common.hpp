@@ -36,6 +36,26 @@ struct Mfma<double> {
   __device__ static inline int row(int lane, int e) { return 4 * e + (lane >> 4); }
 };
 
+// Raw buffer loads: a descriptor covers [base, base + bytes); element offsets past the
+// end read as zero (hardware range check), so guarded loads need no branch and many
+// stay in flight.  Word 3 of the descriptor is the gfx9 raw-buffer configuration.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes > 0 ? bytes : 0), 0x00020000);
+}
+template <typename T>
+__device__ inline T buf_load(rsrc_t r, uint32_t elem);
+template <>
+__device__ inline float buf_load<float>(rsrc_t r, uint32_t elem) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, elem * 4u, 0, 0));
+}
+template <>
+__device__ inline double buf_load<double>(rsrc_t r, uint32_t elem) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, 0, 0);
+  return __hiloint2double((int)v[1], (int)v[0]);
+}
+
 template <typename T>
 struct TileSmem {
   T a[kKc][kTile + kPad];  // op(A) chunk, stored k-major: a[k][i]
@@ -62,39 +82,46 @@ __device__ inline void tile_gemm(const T* A, int64_t lda, const T* B,
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = acc_t{0, 0, 0, 0};
 
+  // operand ranges end at the last valid element, so k-major reads past row k1 are
+  // zero; for i-major views the k-tail is masked explicitly; rows/columns past M/N
+  // read neighbouring data that only feeds outputs which are never stored
+  const int64_t es = sizeof(T);
+  const rsrc_t ra = TA ? make_rsrc(A, ((int64_t)(k1 - 1) * lda + M) * es)
+                       : make_rsrc(A, ((int64_t)(M - 1) * lda + k1) * es);
+  const rsrc_t rb = TB ? make_rsrc(B, ((int64_t)(N - 1) * ldb + k1) * es)
+                       : make_rsrc(B, ((int64_t)(k1 - 1) * ldb + N) * es);
   for (int kb = k0; kb < k1; kb += kKc) {
-    const int kc = (k1 - kb) < kKc ? (k1 - kb) : kKc;
     // stage op(A): 64 x kKc
     if (TA) {
       const int k = tid >> 3, i8 = (tid & 7) * 8;
+      T v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i8 + u;
-        sm.a[k][i] = (k < kc && i < M) ? A[(int64_t)(kb + k) * lda + i] : T(0);
-      }
+      for (int u = 0; u < 8; ++u) v[u] = buf_load<T>(ra, (uint32_t)((int64_t)(kb + k) * lda + i8 + u));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sm.a[k][i8 + u] = v[u];
     } else {
       const int i = tid >> 2, k8 = (tid & 3) * 8;
+      T v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k8 + u;
-        sm.a[k][i] = (k < kc && i < M) ? A[(int64_t)i * lda + kb + k] : T(0);
-      }
+      for (int u = 0; u < 8; ++u) v[u] = buf_load<T>(ra, (uint32_t)((int64_t)i * lda + kb + k8 + u));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sm.a[k8 + u][i] = (kb + k8 + u < k1) ? v[u] : T(0);
     }
     // stage op(B): kKc x 64
     if (TB) {
       const int j = tid >> 2, k8 = (tid & 3) * 8;
+      T v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k8 + u;
-        sm.b[k][j] = (k < kc && j < N) ? B[(int64_t)j * ldb + kb + k] : T(0);
-      }
+      for (int u = 0; u < 8; ++u) v[u] = buf_load<T>(rb, (uint32_t)((int64_t)j * ldb + kb + k8 + u));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sm.b[k8 + u][j] = (kb + k8 + u < k1) ? v[u] : T(0);
     } else {
       const int k = tid >> 3, j8 = (tid & 7) * 8;
+      T v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j8 + u;
-        sm.b[k][j] = (k < kc && j < N) ? B[(int64_t)(kb + k) * ldb + j] : T(0);
-      }
+      for (int u = 0; u < 8; ++u) v[u] = buf_load<T>(rb, (uint32_t)((int64_t)(kb + k) * ldb + j8 + u));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sm.b[k][j8 + u] = v[u];
     }
     __syncthreads();
     const int kr = lane >> 4, cl = lane & 15;
@@ -114,19 +141,25 @@ __device__ inline void tile_gemm(const T* A, int64_t lda, const T* B,
     __syncthreads();
   }
   const int cl = lane & 15;
+  const rsrc_t rc = make_rsrc(C, ((int64_t)(M - 1) * ldc + N) * es);
+  T old[2][2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 32 * wr + 16 * a + Mfma<T>::row(lane, e);
-        const int j = 32 * wc + 16 * b + cl;
-        if (i < M && j < N) {
-          T* p = C + (int64_t)i * ldc + j;
-          const T v = alpha * acc[a][b][e];
-          *p = (beta == T(0)) ? v : v + beta * (*p);
-        }
+        const int i = 32 * wr + 16 * a + Mfma<T>::row(lane, e), j = 32 * wc + 16 * b + cl;
+        old[a][b][e] = (beta == T(0)) ? T(0) : buf_load<T>(rc, (uint32_t)((int64_t)i * ldc + j));
+      }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 32 * wr + 16 * a + Mfma<T>::row(lane, e), j = 32 * wc + 16 * b + cl;
+        if (i < M && j < N) C[(int64_t)i * ldc + j] = alpha * acc[a][b][e] + beta * old[a][b][e];
       }
 }
 

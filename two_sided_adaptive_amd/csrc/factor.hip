@@ -16,6 +16,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "prof.hpp"
 
 namespace g2d {
 namespace {
@@ -34,58 +35,148 @@ __global__ __launch_bounds__(256) void k_reverse_sym(int64_t p, const T* __restr
   Ar[i * p + j] = (double)A[(p - 1 - b) * p + (p - 1 - a)];
 }
 
-// One diagonal 64x64 block: Cholesky in LDS, then its inverse.  Writes L into Ar
-// (lower part), X_kk = L_kk^-1 into X (zeros above the diagonal) and its transpose
-// into DinvT.  Rows beyond p are padded with the identity.
-__global__ __launch_bounds__(64) void k_potrf_diag(int64_t p, int kb, double* __restrict__ Ar,
-                                                   double* __restrict__ X,
-                                                   double* __restrict__ DinvT, int* info,
-                                                   int side_code) {
-  __shared__ double a[NB][NB + 1];
-  __shared__ double x[NB][NB + 1];
+// One diagonal 64x64 block: Cholesky, then its inverse.  Writes L into Ar (lower
+// part), X_kk = L_kk^-1 into X (zeros above the diagonal) and its transpose into DinvT.
+// Rows beyond p are padded with the identity.  256 threads, no branches in the loops.
+//  * Cholesky: thread t owns row i = t/4, columns k = 4u + t%4 (u < 16) in registers.
+//    Step j publishes the still unscaled column j (pivot included) through a double-
+//    buffered LDS column, one barrier, after which every thread applies
+//    a[i][k] -= a[i][j] a[k][j] / a[j][j] to its elements and the owners of column j
+//    scale it by 1/sqrt(a[j][j]).
+//  * Inverse: the quad of threads 4c..4c+3 forward-substitutes column c of L^-1 with
+//    the reciprocal diagonal; thread q keeps the right-hand side of rows 4u + q, and
+//    the new entry x[i][c] is broadcast inside the quad with DPP (no barrier).
+__device__ inline double quad_bcast(double v, int src) {
+  // quad_perm [src, src, src, src] on both 32-bit halves (src is a literal after unrolling)
+  int lo = __double2loint(v), hi = __double2hiint(v);
+  switch (src) {
+    case 0:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0x00, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0x00, 0xF, 0xF, false);
+      break;
+    case 1:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0x55, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0x55, 0xF, 0xF, false);
+      break;
+    case 2:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0xAA, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0xAA, 0xF, 0xF, false);
+      break;
+    default:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0xFF, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0xFF, 0xF, 0xF, false);
+      break;
+  }
+  return __hiloint2double(hi, lo);
+}
+
+// 1/x and 1/sqrt(x) from the hardware estimates refined by one Newton step (a few
+// ulp; the factorisation does not need IEEE-rounded quotients).
+__device__ inline double rcp_nr(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  r = fma(r, fma(-x, r, 1.0), r);
+  return r;
+}
+__device__ inline double rsq_nr(double x) {
+  double r = __builtin_amdgcn_rsq(x);
+  const double h = 0.5 * x * r;
+  r = fma(r, fma(-h, r, 0.5), r);
+  return r;
+}
+
+__global__ __launch_bounds__(256) void k_potrf_diag(int64_t p, int kb, double* __restrict__ Ar,
+                                                    double* __restrict__ X,
+                                                    double* __restrict__ DinvT, int* info,
+                                                    int side_code) {
+  __shared__ double col[2][NB];
+  __shared__ double piv[NB];                // a[j][j] before scaling (for the SPD check)
+  __shared__ double rdiag[NB];              // 1 / L[j][j]
+  __shared__ double lt[NB][4][NB / 4 + 2];  // lt[c][q][u] = L[4u+q][c] (zero above diagonal)
   const int t = threadIdx.x;
+  const int i = t >> 2, q = t & 3;
   const int64_t r0 = (int64_t)kb * NB;
   const int nv = (p - r0) < NB ? (int)(p - r0) : NB;
-  for (int c = 0; c < NB; ++c) {
-    double v;
-    if (t < nv && c < nv)
-      v = (c <= t) ? Ar[(r0 + t) * p + r0 + c] : 0.0;
-    else
-      v = (t == c) ? 1.0 : 0.0;
-    a[t][c] = v;
-    x[t][c] = 0.0;
+  double a[NB / 4];
+  {
+    // all loads in flight together; rows past the matrix read as zero
+    const rsrc_t rr = make_rsrc(Ar + r0 * p + r0, ((int64_t)(nv - 1) * p + nv) * 8);
+#pragma unroll
+    for (int u = 0; u < NB / 4; ++u) a[u] = buf_load<double>(rr, (uint32_t)(i * p + 4 * u + q));
+#pragma unroll
+    for (int u = 0; u < NB / 4; ++u) {
+      const int k = 4 * u + q;
+      const bool in = i < nv && k < nv;
+      a[u] = in ? (k <= i ? a[u] : 0.0) : (i == k ? 1.0 : 0.0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int uj = j >> 2, qj = j & 3;
+    double* cj = col[j & 1];
+    if (q == qj) cj[i] = a[uj];  // column j, unscaled (rows < j hold finished L values)
+    __syncthreads();
+    const double pj = cj[j];
+    const double inv = rcp_nr(pj);
+    const double rs = rsq_nr(pj);
+    const double coef = (i > j) ? cj[i] * inv : 0.0;
+#pragma unroll
+    for (int u = 0; u < NB / 4; ++u) {
+      const int k = 4 * u + q;
+      const double ck = (k > j) ? cj[k] : 0.0;
+      a[u] = fma(-coef, ck, a[u]);
+    }
+    if (q == qj) a[uj] = (i >= j) ? a[uj] * rs : a[uj];
+    if (t == 0) {
+      piv[j] = pj;
+      rdiag[j] = rs;  // 1 / L[j][j]
+    }
+  }
+  // publish L (transposed, quad-split, zero above the diagonal) for the inverse
+#pragma unroll
+  for (int u = 0; u < NB / 4; ++u) {
+    const int k = 4 * u + q;
+    lt[k][i & 3][i >> 2] = (k <= i) ? a[u] : 0.0;
   }
   __syncthreads();
-  int bad = -1;
-  for (int j = 0; j < NB; ++j) {
-    double d = a[j][j];
-    if (!(d > 0.0) && bad < 0) bad = j;
-    d = sqrt(d);
-    __syncthreads();
-    if (t == j) a[j][j] = d;
-    if (t > j) a[t][j] = a[t][j] / d;
-    __syncthreads();
-    if (t > j) {
-      const double lij = a[t][j];
-      for (int k = j + 1; k <= t; ++k) a[t][k] -= lij * a[k][j];
-    }
-    __syncthreads();
+  if (t < 64) {  // first non-positive (or NaN) pivot, found by one wave
+    const bool bad = t < nv && !(piv[t] > 0.0);
+    const unsigned long long mask = __ballot(bad);
+    if (t == 0 && mask != 0ull) record_info(info, side_code, (int)(r0 + __ffsll((long long)mask)));
   }
-  // X = L^-1, row by row: x[i][c] = (delta_ic - sum_{k<i} a[i][k] x[k][c]) / a[i][i]
-  for (int i = 0; i < NB; ++i) {
-    double s = (i == t) ? 1.0 : 0.0;
-    for (int k = 0; k < i; ++k) s -= a[i][k] * x[k][t];
-    if (t <= i) x[i][t] = s / a[i][i];
-    __syncthreads();
-  }
-  if (t < nv) {
-    for (int c = 0; c < nv; ++c) {
-      if (c <= t) Ar[(r0 + t) * p + r0 + c] = a[t][c];
-      X[(r0 + t) * p + r0 + c] = x[t][c];
+  if (i < nv) {
+#pragma unroll
+    for (int u = 0; u < NB / 4; ++u) {
+      const int k = 4 * u + q;
+      if (k <= i && k < nv) Ar[(r0 + i) * p + r0 + k] = a[u];
     }
   }
-  for (int c = 0; c < NB; ++c) DinvT[(int64_t)kb * NB * NB + (int64_t)c * NB + t] = x[t][c];
-  if (t == 0 && bad >= 0 && bad < nv) record_info(info, side_code, (int)(r0 + bad + 1));
+  __syncthreads();
+  // inverse: quad c = t/4 solves column c
+  const int c = i;
+  double rhs[NB / 4], xv[NB / 4];
+#pragma unroll
+  for (int u = 0; u < NB / 4; ++u) {
+    rhs[u] = (4 * u + q == c) ? 1.0 : 0.0;
+    xv[u] = 0.0;
+  }
+#pragma unroll
+  for (int r = 0; r < NB; ++r) {
+    const int ur = r >> 2, qr = r & 3;
+    double x = quad_bcast(rhs[ur] * rdiag[r], qr);  // meaningful in lane q == qr
+    x = (r < c) ? 0.0 : x;
+    xv[ur] = (q == qr) ? x : xv[ur];
+    const double* lr = &lt[r][q][0];
+#pragma unroll
+    for (int u = 0; u < NB / 4; ++u) rhs[u] = fma(-lr[u], x, rhs[u]);
+  }
+  // X rows 4u+q, column c; DinvT[c][row] = X[row][c]
+  double* dt = DinvT + (int64_t)kb * NB * NB + (int64_t)c * NB;
+#pragma unroll
+  for (int u = 0; u < NB / 4; ++u) {
+    const int row = 4 * u + q;
+    dt[row] = xv[u];
+    if (row < nv && c < nv) X[(r0 + row) * p + r0 + c] = xv[u];
+  }
 }
 
 // Panel solve L[i][kb] = A[i][kb] (L_kk^-1)^T for row tiles below the diagonal block.
@@ -204,33 +295,85 @@ size_t factor_workspace(int64_t p) {
          align_up((size_t)p * ldt * sizeof(double));
 }
 
+// Dense GEMM flops of one launch (only evaluated while the measurement hook is on).
+double trailing_flops(int64_t p, int kb) {
+  const int64_t nblk = cdiv(p, NB);
+  const double K = (double)((p - kb * NB) < NB ? (p - kb * NB) : NB);
+  double f = 0.0;
+  for (int64_t i = kb + 1; i < nblk; ++i) {
+    const double M = (double)((p - i * NB) < NB ? (p - i * NB) : NB);
+    for (int64_t j = kb + 1; j <= i; ++j) {
+      const double N = (double)((p - j * NB) < NB ? (p - j * NB) : NB);
+      f += 2.0 * M * N * K;
+    }
+  }
+  return f;
+}
+
+void trtri_flops(int64_t p, int64_t h, double* f1, double* f2) {
+  *f1 = *f2 = 0.0;
+  for (int64_t g0 = 0; g0 < p; g0 += 2 * h) {
+    const int64_t h1 = (p - g0) < h ? (p - g0) : h;
+    const int64_t h2 = (p - g0 - h) < h ? (p - g0 - h) : h;
+    if (h2 <= 0) continue;
+    for (int64_t ti = 0; ti * NB < h2; ++ti) {
+      const double M = (double)((h2 - ti * NB) < NB ? (h2 - ti * NB) : NB);
+      const double kend = (double)((ti + 1) * NB < h2 ? (ti + 1) * NB : h2);
+      for (int64_t tj = 0; tj * NB < h1; ++tj) {
+        const double N = (double)((h1 - tj * NB) < NB ? (h1 - tj * NB) : NB);
+        *f1 += 2.0 * M * N * (double)(h1 - tj * NB);
+        *f2 += 2.0 * M * N * kend;
+      }
+    }
+  }
+}
+
 hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws, int* info,
                           int side_code, hipStream_t s) {
   FactorWs f = carve(p, ws);
   const int64_t nblk = cdiv(p, NB);
+  const bool pr = prof_on();
+  const double es = dtype == 0 ? 4.0 : 8.0, pp = (double)p * (double)p;
   dim3 eg((unsigned)cdiv(p, 64), (unsigned)cdiv(p, 4));
+  prof_begin(KC_OTHER, s);
   if (dtype == 0)
     k_reverse_sym<float><<<eg, 256, 0, s>>>(p, (const float*)A, f.Ar);
   else
     k_reverse_sym<double><<<eg, 256, 0, s>>>(p, (const double*)A, f.Ar);
+  prof_end(KC_OTHER, s, 0.0, pp * (es + 8.0));
   for (int kb = 0; kb < nblk; ++kb) {
-    k_potrf_diag<<<1, 64, 0, s>>>(p, kb, f.Ar, f.X, f.DinvT, info, side_code);
+    const double nv = (double)((p - kb * NB) < NB ? (p - kb * NB) : NB);
+    prof_begin(KC_POTRF, s);
+    k_potrf_diag<<<1, 256, 0, s>>>(p, kb, f.Ar, f.X, f.DinvT, info, side_code);
+    prof_end(KC_POTRF, s, 2.0 / 3.0 * nv * nv * nv, 8.0 * (nv * nv * 2.5 + NB * NB));
     const int rest = (int)(nblk - kb - 1);
     if (rest > 0) {
+      const double rows = (double)(p - (int64_t)(kb + 1) * NB);
+      prof_begin(KC_PANEL, s);
       k_panel_solve<<<rest, 256, 0, s>>>(p, kb, f.Ar, f.DinvT);
+      prof_end(KC_PANEL, s, 2.0 * rows * nv * nv, 8.0 * (2.0 * rows * nv + nv * nv));
+      prof_begin(KC_TRAILING, s);
       k_trailing<<<dim3(rest, rest), 256, 0, s>>>(p, kb, f.Ar);
+      prof_end(KC_TRAILING, s, pr ? trailing_flops(p, kb) : 0.0,
+               8.0 * (rows * (rows + NB) + rows * nv));
     }
   }
   for (int64_t h = NB; h < p; h *= 2) {
     const int64_t groups = cdiv(p, 2 * h);
     dim3 g((unsigned)cdiv(h, NB), (unsigned)cdiv(h, NB), (unsigned)groups);
+    double f1 = 0.0, f2 = 0.0;
+    if (pr) trtri_flops(p, h, &f1, &f2);
+    prof_begin(KC_TRTRI, s);
     k_trtri_step1<<<g, 256, 0, s>>>(p, h, f.Ar, f.X, f.Tb, f.ldt);
     k_trtri_step2<<<g, 256, 0, s>>>(p, h, f.X, f.Tb, f.ldt);
+    prof_end(KC_TRTRI, s, f1 + f2, 8.0 * 4.0 * (double)h * (double)p);
   }
+  prof_begin(KC_OTHER, s);
   if (dtype == 0)
     k_finalize<float><<<eg, 256, 0, s>>>(p, f.X, (float*)U);
   else
     k_finalize<double><<<eg, 256, 0, s>>>(p, f.X, (double*)U);
+  prof_end(KC_OTHER, s, 0.0, pp * (8.0 / 2.0 + es));
   return hipGetLastError();
 }
 

@@ -4,11 +4,19 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace g2d {
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Library-owned per-device resources: a second stream (default priority) and a pool
+// of timing-disabled events.  Callers must hold lib_mutex() from the first use of
+// the events until the last wait that names them has been enqueued.
+std::recursive_mutex& lib_mutex();
+hipError_t aux_resources(size_t nevents, hipStream_t* aux, hipEvent_t** events);
 
 // Factor stage (factor.hip): U' (dtype) of one SPD matrix A (dtype), fp64 inside.
 size_t factor_workspace(int64_t p);
