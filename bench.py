@@ -18,11 +18,57 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK = {"hbm_gbs": 8000.0, "fp32_tflops": 157.3, "fp64_tflops": 78.6}
+# Kernel sources whose text the stored HBM-traffic counters belong to.
+TRAFFIC_SOURCES = ("two_sided_adaptive_amd/csrc/sweep.hip", "two_sided_adaptive_amd/csrc/common.hpp")
 METRIC = "quantized weight entries/sec and s/layer, 4096x4096 4-bit GPTQ-2D, 1 MI355X"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload, dtype):
+    """HBM bytes per launch of the rounding kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy kernel), or None when the summary
+    is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"pmc_round_{workload.lower()}_{dtype}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("#", "|", " ")):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    """A plain elementwise copy of known size (reads and writes `mib` MiB once each), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "bytes_read": 4 * n, "bytes_written": 4 * n,
+                      "kernel": "torch.neg (elementwise)", "dispatches": 3}), flush=True)
 
 
 def cpu_baseline(wl, W, A, B, s, z_gpu, rows):
@@ -71,6 +117,8 @@ def main():
     ap.add_argument("--no-alt", action="store_true", help="skip timing the other sweep dtype")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -88,6 +136,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     g2d.load_library()
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -135,6 +186,7 @@ def main():
             "avg_launch_us": 1e3 * ms / launches,
             "tflops": flops / sec / 1e12 if sec > 0 else None,
             "gbs": byts / sec / 1e9 if sec > 0 else None,
+            "bytes_per_launch": byts / launches, "flops_per_launch": flops / launches,
         }
     log("[bench] per-kernel: " + json.dumps(kernels))
     gemm_peak = PEAK["fp32_tflops"] if args.dtype == "f32" else PEAK["fp64_tflops"]
@@ -149,8 +201,10 @@ def main():
             return {"kernel": name, "bound": "mfma", "achieved": k["tflops"],
                     "peak": PEAK["fp64_tflops"], "unit": "TFLOP/s",
                     "frac": k["tflops"] / PEAK["fp64_tflops"], "traffic": None}
+        traffic = stored_traffic(wl.name, args.dtype) if name == "round" else None
         return {"kernel": name, "bound": "hbm", "achieved": k["gbs"], "peak": PEAK["hbm_gbs"],
-                "unit": "GB/s", "frac": k["gbs"] / PEAK["hbm_gbs"], "traffic": None}
+                "unit": "GB/s", "frac": k["gbs"] / PEAK["hbm_gbs"], "traffic": traffic,
+                "algorithmic_bytes_per_launch": k["bytes_per_launch"]}
 
     z_gpu = codes.cpu().numpy().astype(np.int32)
     alt = None

@@ -584,7 +584,7 @@ __global__ __launch_bounds__(256) void k_check_scales(int64_t m, const T* __rest
 // Algorithmic work of one launch (only evaluated while the measurement hook is on).
 // Round: in-block feedback flops, the two 64-deep neighbour pulls (2 M N K), and the
 // HBM bytes every block must move (W, Vf, Hf, the neighbour panels, the diagonal
-// factor blocks and scales in; R, Delta, Q, codes out).
+// factor blocks and scales in; R, Delta, Q out, one byte per code).
 void round_work(int64_t m, int64_t n, int D, int Mb, int Nb, double es, double* flops,
                 double* bytes) {
   *flops = *bytes = 0.0;
@@ -595,7 +595,7 @@ void round_work(int64_t m, int64_t n, int D, int Mb, int Nb, double es, double* 
     const double mr = (double)((m - (int64_t)K * BB) < BB ? (m - (int64_t)K * BB) : BB);
     const double nc = (double)((n - (int64_t)L * BB) < BB ? (n - (int64_t)L * BB) : BB);
     *flops += mr * nc * (mr + nc - 2.0);
-    *bytes += es * (7.0 * mr * nc + mr * mr + nc * nc + mr) + mr * nc;
+    *bytes += es * (6.0 * mr * nc + mr * mr + nc * nc + mr) + mr * nc;
     if (K > 0) {
       *flops += 2.0 * mr * nc * BB;
       *bytes += es * (BB * mr + BB * nc);
