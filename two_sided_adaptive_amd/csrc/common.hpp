@@ -55,6 +55,18 @@ __device__ inline double buf_load<double>(rsrc_t r, uint32_t elem) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, 0, 0);
   return __hiloint2double((int)v[1], (int)v[0]);
 }
+// Same with a wave-uniform element offset `uelem` added through the scalar offset field.
+template <typename T>
+__device__ inline T buf_load_s(rsrc_t r, uint32_t elem, uint32_t uelem);
+template <>
+__device__ inline float buf_load_s<float>(rsrc_t r, uint32_t elem, uint32_t uelem) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, elem * 4u, uelem * 4u, 0));
+}
+template <>
+__device__ inline double buf_load_s<double>(rsrc_t r, uint32_t elem, uint32_t uelem) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, uelem * 8u, 0);
+  return __hiloint2double((int)v[1], (int)v[0]);
+}
 
 template <typename T>
 struct TileSmem {

@@ -83,6 +83,7 @@ struct RoundSmem {
   T h0s[4][MU][MU];      // per wave, skewed: H pushed from outside; scratch during a sweep
   T sc[BB];              // scales
   T rs[BB];              // fl(1 / scale)
+  T sup[BB][2];          // sup[c] = (U'b[c-2][c], U'b[c-1][c]) inside c's micro-tile
   int8_t zz[BB][BB];     // codes of this block
 };
 
@@ -167,6 +168,30 @@ __device__ inline Vec4<double> lds_read4(const double* p) {
   const d2 y = *(const d2*)(p + 2);
   return Vec4<double>{{x[0], x[1], y[0], y[1]}};
 }
+// Two consecutive elements (aligned to their pair size).
+template <typename T>
+struct Vec2 {
+  T v[2];
+};
+__device__ inline Vec2<float> lds_read2(const float* p) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 x = *(const f2*)p;
+  return Vec2<float>{{x[0], x[1]}};
+}
+__device__ inline Vec2<double> lds_read2(const double* p) {
+  typedef double d2 __attribute__((ext_vector_type(2)));
+  const d2 x = *(const d2*)p;
+  return Vec2<double>{{x[0], x[1]}};
+}
+
+// LDS operands of one step of the micro sweep for lane (r, q) at column l: the quarter's
+// four R values of column l (rows 4q..4q+3), its four Delta values of row r and the four
+// U'b entries of column l (rows 4q..4q+3), and the two superdiagonal factors of column l.
+template <typename T>
+struct StepOps {
+  Vec4<T> rv, dv, bv;
+  Vec2<T> sp;
+};
 
 // Rounds all blocks of block anti-diagonal D.  Wave w owns micro-row w (16 rows) and at
 // micro anti-diagonal d handles micro-tile (w, d - w).  In the micro sweep, lane
@@ -299,6 +324,13 @@ __global__ __launch_bounds__(256) void k_round(SweepArgs<T> a, int D) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) hin[jm][e] += acc[jm][e];
   }
+  // coupling to columns of an earlier micro-tile is applied by the MFMA pulls, so the
+  // table is zero where l-1 or l-2 falls outside l's micro-tile
+  if (tid < BB) {
+    const int lm = tid & (MU - 1);
+    sm.sup[tid][0] = lm >= 2 ? sm.ubT[tid][tid - 2] : T(0);
+    sm.sup[tid][1] = lm >= 1 ? sm.ubT[tid][tid - 1] : T(0);
+  }
   __syncthreads();
   // the staging areas become this block's R and Delta, which start at zero
 #pragma unroll
@@ -321,6 +353,7 @@ __global__ __launch_bounds__(256) void k_round(SweepArgs<T> a, int D) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) cu[u] = sm.ua[MU * w + 4 * qq + u][gr];
   const T cup = (rr_ > 0) ? sm.ua[gr - 1][gr] : T(0);
+  const T cup2 = (rr_ > 1) ? sm.ua[gr - 2][gr] : T(0);
 
   for (int d = 0; d < 2 * (BB / MU) - 1; ++d) {
     const int j = d - w;  // micro-column of this wave's micro-tile (wave-uniform)
@@ -361,7 +394,7 @@ __global__ __launch_bounds__(256) void k_round(SweepArgs<T> a, int D) {
         sm.h0s[w][row][(col + row) & (MU - 1)] = hv[e] + (ah0[e] + ah1[e]);
       }
       lds_wave_sync();
-      T g0r[MU], h0r[MU], sdr[MU];
+      T g0r[MU], h0r[MU];
 #pragma unroll
       for (int sl = 0; sl < MU; sl += 4) {
         const Vec4<T> gv = lds_read4(&sm.g0s[w][rr_][sl]);
@@ -372,34 +405,45 @@ __global__ __launch_bounds__(256) void k_round(SweepArgs<T> a, int D) {
           h0r[sl + u] = hv4.v[u];
         }
       }
-#pragma unroll
-      for (int sl = 0; sl < MU; ++sl) {
-        const int col = (sl - rr_) & (MU - 1);
-        sdr[sl] = col > 0 ? sm.ubT[mc0 + col][mc0 + col - 1] : T(0);  // U'b[l-1][l]
-      }
-      lds_wave_sync();
       const T* rtq = &sm.rT[mc0][MU * w + 4 * qq];  // + P * column
       const T* ddq = &sm.dd[gr][mc0 + 4 * qq];
       const T* ubq = &sm.ubT[mc0][mc0 + 4 * qq];    // + P * column
+      const T* spq = &sm.sup[mc0][0];                // + 2 * column
+      // Operands of step st are read during step st - 2.  At that point rows <= r - 3
+      // (columns <= l - 3) are written and the two nearer ones still read as zero, so
+      // the LDS sums hold exactly the older terms; rows r-1, r-2 and columns l-1, l-2
+      // are added from registers (DPP row shifts and the lane's own previous Deltas).
+      auto fetch = [&](int st2) {
+        const int l2 = st2 - rr_;
+        const int lc = (l2 >= 0 && l2 < MU) ? l2 : 0;
+        StepOps<T> o;
+        o.rv = lds_read4(rtq + P * lc);
+        o.dv = lds_read4(ddq);
+        o.bv = lds_read4(ubq + P * lc);
+        o.sp = lds_read2(spq + 2 * lc);
+        return o;
+      };
+      StepOps<T> x0 = fetch(0);
+      StepOps<T> x1 = fetch(1);
+      lds_wave_sync();
       // inactive lanes store into this wave's staging row, which is dead until the
       // next micro-tile
       T* dummy = &sm.h0s[w][rr_][0];
       T pv = T(0), ph = T(0);
-      T rprev = T(0), dprev = T(0);
+      T rprev = T(0), rup = T(0), dprev = T(0), dprev2 = T(0);
 #pragma unroll
       for (int st = 0; st < 2 * MU - 1; ++st) {
         const int l = st - rr_;
         const bool act = (l >= 0) && (l < MU);
-        // (A) operands of the next step's older-term sums (written up to step st-1)
-        const int l1 = st + 1 - rr_;
-        const int lc1 = (l1 >= 0 && l1 < MU) ? l1 : 0;
-        const Vec4<T> rv = lds_read4(rtq + P * lc1);
-        const Vec4<T> dv = lds_read4(ddq);
-        const Vec4<T> bv = lds_read4(ubq + P * lc1);
-        // (B) critical chain of this step
-        const T rup = up_row(rprev);
-        const T g = g0r[st & (MU - 1)] - (pv + cup * rup);
-        const T hh = h0r[st & (MU - 1)] + (ph + sdr[st & (MU - 1)] * dprev);
+        // (A) operands two steps ahead
+        StepOps<T> x2;
+        if (st + 2 < 2 * MU - 1) x2 = fetch(st + 2);
+        // (B) critical chain of this step; the second-nearest terms are ready early
+        const T pv2 = pv + cup2 * up_row(rup);      // + U'a[r-2][r] R[r-2][l]
+        const T ph2 = ph + x0.sp.v[0] * dprev2;     // + Delta[r][l-2] U'b[l-2][l]
+        rup = up_row(rprev);                        // R[r-1][l]
+        const T g = g0r[st & (MU - 1)] - (pv2 + cup * rup);
+        const T hh = h0r[st & (MU - 1)] + (ph2 + x0.sp.v[1] * dprev);
         const T t = g - hh;
         T z = round_quot(t, s_r, rs_r, tol);
         z = min_t(max_t(z, tlo), thi);
@@ -413,16 +457,21 @@ __global__ __launch_bounds__(256) void k_round(SweepArgs<T> a, int D) {
         *pdd = dv_new;
         *pzz = (int8_t)(int)z;
         rprev = rv_new;
+        dprev2 = dprev;
         dprev = dv_new;
-        // (C) older-term sums of the next step
-        T sv = T(0), sh = T(0);
+        // (C) the next step's terms other than its nearest row and column
+        if (st + 1 < 2 * MU - 1) {
+          T sv = T(0), sh = T(0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          sv += cu[u] * rv.v[u];
-          sh += dv.v[u] * bv.v[u];
+          for (int u = 0; u < 4; ++u) {
+            sv += cu[u] * x1.rv.v[u];
+            sh += x1.dv.v[u] * x1.bv.v[u];
+          }
+          pv = quad_sum(sv);
+          ph = quad_sum(sh);
         }
-        pv = quad_sum(sv);
-        ph = quad_sum(sh);
+        x0 = x1;
+        x1 = x2;
         lds_wave_sync();
       }
     }
@@ -443,133 +492,231 @@ __global__ __launch_bounds__(256) void k_round(SweepArgs<T> a, int D) {
   }
 }
 
-// One 64x64 output tile, C[i][j] += alpha * sum_{k<K} A[k*lda + i] * B[k*ldb + j]
-// (both operands k-major).  Four waves in a 2x2 arrangement, each 32x32 = 2x2 MFMA
-// tiles; operand fragments are read straight from global memory (16 consecutive
-// elements per k, coalesced) into a ring of PF k-steps kept in flight ahead of the
-// MFMAs that use them.  All loads are branch-free (clamped address, zero select).
+// Depth of one LDS stage of the push GEMM: 32 doubles or 64 floats per chunk of k-rows,
+// so both element types stage the same number of bytes.
 template <typename T>
-__device__ inline void tile_tn(const T* A, int64_t lda, const T* B, int64_t ldb, T* C,
-                               int64_t ldc, int M, int N, int K, T alpha) {
+struct PushKc;
+template <>
+struct PushKc<float> {
+  static constexpr int v = 64;
+};
+template <>
+struct PushKc<double> {
+  static constexpr int v = 32;
+};
+// LDS row strides (elements) of the staged operands: a multiple of 16 plus 16, so the
+// four k-rows read by one MFMA operand load start 32 dwords (f64) or 16 dwords (f32)
+// apart and fall in different banks.
+constexpr int kPadWide = 256 + 16;  // 256-wide operand
+constexpr int kPadNarrow = 64 + 16;  // 64-wide operand
+constexpr int kPushThreads = 512;
+template <typename T>
+struct PushSmem {
+  static constexpr int KC = PushKc<T>::v;
+  T buf[KC * (kPadWide + kPadNarrow)];  // A rows, then B rows
+  int task;
+};
+
+// G[x][y] = sum_{k<K} A[k*lda + x] B[k*ldb + y] for x < M <= 256, y < N <= 64, both
+// operands k-major, added into C: C[x*ldc + y] += G[x][y], or with `trans`
+// C[y*ldc + x] += G[x][y].  One workgroup of eight waves, two per SIMD; wave w owns rows
+// x in [32w, 32w+32) as 2x4 MFMA tiles.  Operands are staged through LDS KC k-rows at a
+// time, with the next chunk's global loads in flight in registers while the current
+// chunk is multiplied.  k-rows past K read as zero (exact buffer ranges); rows or
+// columns past M, N read neighbouring finite data that only reaches outputs that are
+// never stored.  The transposed update goes through LDS so that its stores are
+// coalesced along x.
+template <typename T>
+__device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t ldb, T* C,
+                                  int64_t ldc, int M, int N, int K, bool trans,
+                                  PushSmem<T>& sm) {
   typedef typename Mfma<T>::acc_t acc_t;
-  constexpr int PF = 4;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int i0 = 32 * (w >> 1), j0 = 32 * (w & 1);
-  const int kq = lane >> 4, c = lane & 15;
+  constexpr int BM = 256, BN = 64;
+  constexpr int KC = PushKc<T>::v;
+  constexpr int SA = kPadWide, SB = kPadNarrow;
+  constexpr int TH = kPushThreads;
+  constexpr int NA = KC * BM / TH, NB = KC * BN / TH;  // staged elements per thread
+  constexpr int TM = 2, TN = 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wi0 = 32 * w;
+  const int kq = lane >> 4, cl = lane & 15;
   const int64_t es = sizeof(T);
-  // k-major views end after row K: reads of k >= K are zero.  Rows/columns past M/N
-  // read neighbouring data that only reaches outputs which are never stored.
   const rsrc_t ra = make_rsrc(A, ((int64_t)(K - 1) * lda + M) * es);
   const rsrc_t rb = make_rsrc(B, ((int64_t)(K - 1) * ldb + N) * es);
-  const rsrc_t rc = make_rsrc(C, ((int64_t)(M - 1) * ldc + N) * es);
-  acc_t acc[2][2];
+  const int nch = (K + KC - 1) / KC;
+  // thread tid stages elements tid + TH u of each chunk: k-row tid / BM + u (TH / BM),
+  // column tid % BM; the per-u and per-chunk parts of the offset are wave-uniform
+  const uint32_t va = (uint32_t)((tid / BM) * lda + tid % BM);
+  const uint32_t vb = (uint32_t)((tid / BN) * ldb + tid % BN);
+  T pa[NA], pb[NB];
+  auto fetch = [&](int c) {
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+    for (int u = 0; u < NA; ++u)
+      pa[u] = buf_load_s<T>(ra, va, (uint32_t)((c * KC + u * (TH / BM)) * lda));
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = acc_t{0, 0, 0, 0};
-  T fa[PF][2], fb[PF][2];
-  auto fetch = [&](int slot, int k) {
-    const uint32_t oa = (uint32_t)((int64_t)k * lda + i0 + c);
-    const uint32_t ob = (uint32_t)((int64_t)k * ldb + j0 + c);
-    fa[slot][0] = buf_load<T>(ra, oa);
-    fa[slot][1] = buf_load<T>(ra, oa + 16);
-    fb[slot][0] = buf_load<T>(rb, ob);
-    fb[slot][1] = buf_load<T>(rb, ob + 16);
+    for (int u = 0; u < NB; ++u)
+      pb[u] = buf_load_s<T>(rb, vb, (uint32_t)((c * KC + u * (TH / BN)) * ldb));
   };
+  T* const as0 = sm.buf + (tid / BM) * SA + tid % BM;
+  T* const bs0 = sm.buf + SA * KC + (tid / BN) * SB + tid % BN;
+  auto stage = [&]() {
 #pragma unroll
-  for (int sl = 0; sl < PF; ++sl) fetch(sl, 4 * sl + kq);
-  for (int k0 = 0; k0 < K; k0 += 4 * PF) {
+    for (int u = 0; u < NA; ++u) as0[u * (TH / BM) * SA] = pa[u];
 #pragma unroll
-    for (int sl = 0; sl < PF; ++sl) {
-      const T a0 = fa[sl][0], a1 = fa[sl][1], b0 = fb[sl][0], b1 = fb[sl][1];
-      fetch(sl, k0 + 4 * (sl + PF) + kq);
-      acc[0][0] = Mfma<T>::run(a0, b0, acc[0][0]);
-      acc[0][1] = Mfma<T>::run(a0, b1, acc[0][1]);
-      acc[1][0] = Mfma<T>::run(a1, b0, acc[1][0]);
-      acc[1][1] = Mfma<T>::run(a1, b1, acc[1][1]);
+    for (int u = 0; u < NB; ++u) bs0[u * (TH / BN) * SB] = pb[u];
+  };
+  acc_t acc[TM][TN];
+#pragma unroll
+  for (int x = 0; x < TM; ++x)
+#pragma unroll
+    for (int y = 0; y < TN; ++y) acc[x][y] = acc_t{0, 0, 0, 0};
+  auto multiply = [&]() {
+    const T* as = sm.buf;
+    const T* bs = sm.buf + SA * KC;
+#pragma unroll 2
+    for (int ks = 0; ks < KC / 4; ++ks) {
+      T fa[TM], fb[TN];
+#pragma unroll
+      for (int x = 0; x < TM; ++x) fa[x] = as[(4 * ks + kq) * SA + wi0 + 16 * x + cl];
+#pragma unroll
+      for (int y = 0; y < TN; ++y) fb[y] = bs[(4 * ks + kq) * SB + 16 * y + cl];
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y) acc[x][y] = Mfma<T>::run(fa[x], fb[y], acc[x][y]);
     }
+  };
+  fetch(0);
+  stage();
+  __syncthreads();
+  // no branches in the loop body (keeps the accumulators in place); the fetch after the
+  // last chunk reads past K, i.e. zeros, without touching memory
+  for (int c = 0; c < nch; ++c) {
+    fetch(c + 1);
+    multiply();
+    __syncthreads();
+    stage();
+    __syncthreads();
   }
-  T old[2][2][4];
+  if (!trans) {
+    const rsrc_t rc = make_rsrc(C, ((int64_t)(M - 1) * ldc + N) * es);
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < TM; ++x) {
+      T old[TN][4];
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+      for (int y = 0; y < TN; ++y)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i0 + 16 * x + Mfma<T>::row(lane, e), j = j0 + 16 * y + c;
-        old[x][y][e] = buf_load<T>(rc, (uint32_t)((int64_t)i * ldc + j));
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int i = wi0 + 16 * x + Mfma<T>::row(lane, e), j = 16 * y + cl;
+          old[y][e] = buf_load<T>(rc, (uint32_t)((int64_t)i * ldc + j));
+        }
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+      for (int y = 0; y < TN; ++y)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+        for (int e = 0; e < 4; ++e) {
+          const int i = wi0 + 16 * x + Mfma<T>::row(lane, e), j = 16 * y + cl;
+          if (i < M && j < N) C[(int64_t)i * ldc + j] = old[y][e] + acc[x][y][e];
+        }
+    }
+    return;
+  }
+  // transposed: two halves of 128 x-values; the owners write G^T into LDS (pitch 130),
+  // then every thread updates whole C rows
+  constexpr int PT = 128 + 2;
+  const rsrc_t rc = make_rsrc(C, ((int64_t)(N - 1) * ldc + M) * es);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i0 + 16 * x + Mfma<T>::row(lane, e), j = j0 + 16 * y + c;
-        if (i < M && j < N) C[(int64_t)i * ldc + j] = old[x][y][e] + alpha * acc[x][y][e];
-      }
+  for (int h = 0; h < 2; ++h) {
+    if ((w >> 2) == h) {
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int xi = wi0 - 128 * h + 16 * x + Mfma<T>::row(lane, e), yj = 16 * y + cl;
+            sm.buf[yj * PT + xi] = acc[x][y][e];
+          }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int u = 0; u < 64 * 128 / TH; ++u) {
+      const int idx = tid + TH * u, yj = idx >> 7, xi = idx & 127;
+      const int x = 128 * h + xi;
+      const T old = buf_load<T>(rc, (uint32_t)((int64_t)yj * ldc + x));
+      if (x < M && yj < N) C[(int64_t)yj * ldc + x] = old + sm.buf[yj * PT + xi];
+    }
+    __syncthreads();
+  }
 }
 
-// Band pushes of the blocks on diagonal D that the next diagonal does not pull
-// itself.  z = 0: vertical into Vf from block (K, L) to row block t = K+2+x of column L;
-// z = 1: horizontal into Hf from (K, L) to column block t = L+2+x of row K.  Targets up
-// to the first block of the next outer block take the 64-deep panel of (K, L); beyond
-// that, a block that closes an outer block pushes the whole outer block (256 deep).
+// Band pushes of the blocks on diagonal D that later diagonals do not pull themselves.
+// Vertical (into Vf) from block (K, L) to row blocks t >= K+2 of column L, horizontal
+// (into Hf) from (K, L) to column blocks t >= L+2 of row K.  Targets up to the first
+// block of the next outer block take the 64-deep panel of (K, L) (one "near" panel of at
+// most three targets); beyond that, a block that closes an outer block pushes the whole
+// outer block, 256 deep, in panels of four targets.  Workgroups take tasks (panel,
+// direction, source block) from a queue, far panels first; each target tile is written
+// by one task, so the order of tasks does not matter for the result.
 template <typename T>
-__global__ __launch_bounds__(256) void k_push(SweepArgs<T> a, int D) {
+__global__ __launch_bounds__(kPushThreads) void k_push(SweepArgs<T> a, int D, int ntask, int P,
+                                                       int* queue) {
+  __shared__ PushSmem<T> sm;
   const int kmin = D - (a.Nb - 1) > 0 ? D - (a.Nb - 1) : 0;
-  const int K = kmin + blockIdx.y;
-  const int L = D - K;
+  const int nblk2 = ntask / P;  // source blocks x 2 directions
   const int64_t m = a.m, n = a.n;
-  if (blockIdx.z == 0) {
-    const int t = K + 2 + blockIdx.x;
-    if (t >= a.Mb) return;
+  for (;;) {
+    __syncthreads();  // sm.task and the staging area are free
+    if (threadIdx.x == 0) sm.task = atomicAdd(queue + D, 1);
+    __syncthreads();
+    const int task = sm.task;
+    if (task >= ntask) break;
+    const int panel = P - 1 - task / nblk2, rest = task % nblk2, dir = rest & 1;
+    const int K = kmin + (rest >> 1), L = D - K;
+    const int own = dir == 0 ? K : L;                // source block index along the push
+    const int nt = dir == 0 ? a.Mb : a.Nb;           // blocks along the push
+    const int first_next = GOUT * (own / GOUT + 1);  // first block of the next outer block
+    const int64_t ext = dir == 0 ? m : n;
+    int t0, t1, ks;
     int64_t src0;
-    int ks;
-    if (t <= GOUT * (K / GOUT + 1)) {
-      src0 = (int64_t)K * BB;
-      ks = (m - src0) < BB ? (int)(m - src0) : BB;
-    } else if (K % GOUT == GOUT - 1) {
-      src0 = (int64_t)(K - (GOUT - 1)) * BB;
-      ks = GOUT * BB;
+    if (panel == 0) {
+      t0 = own + 2;
+      t1 = first_next < nt - 1 ? first_next : nt - 1;
+      src0 = (int64_t)own * BB;
+      ks = (ext - src0) < BB ? (int)(ext - src0) : BB;
     } else {
-      return;
-    }
-    const int64_t tr0 = (int64_t)t * BB, c0 = (int64_t)L * BB;
-    const int M = (m - tr0) < BB ? (int)(m - tr0) : BB;
-    const int N = (n - c0) < BB ? (int)(n - c0) : BB;
-    tile_tn<T>(a.Ua + src0 * m + tr0, m, a.R + src0 * n + c0, n, a.Vf + tr0 * n + c0, n, M, N, ks,
-               T(1));
-  } else {
-    const int t = L + 2 + blockIdx.x;
-    if (t >= a.Nb) return;
-    int64_t src0;
-    int ks;
-    if (t <= GOUT * (L / GOUT + 1)) {
-      src0 = (int64_t)L * BB;
-      ks = (n - src0) < BB ? (int)(n - src0) : BB;
-    } else if (L % GOUT == GOUT - 1) {
-      src0 = (int64_t)(L - (GOUT - 1)) * BB;
+      if (own % GOUT != GOUT - 1) continue;
+      t0 = first_next + 1 + 4 * (panel - 1);
+      t1 = t0 + 3 < nt - 1 ? t0 + 3 : nt - 1;
+      src0 = (int64_t)(own - (GOUT - 1)) * BB;
       ks = GOUT * BB;
-    } else {
-      return;
     }
-    const int64_t r0 = (int64_t)K * BB, tc0 = (int64_t)t * BB;
-    const int M = (m - r0) < BB ? (int)(m - r0) : BB;
-    const int N = (n - tc0) < BB ? (int)(n - tc0) : BB;
-    tile_tn<T>(a.DT + src0 * m + r0, m, a.Ub + src0 * n + tc0, n, a.Hf + r0 * n + tc0, n, M, N, ks,
-               T(1));
+    if (t0 > t1) continue;
+    const int64_t p0 = (int64_t)t0 * BB;  // first pushed row (dir 0) or column (dir 1)
+    const int64_t pend = (int64_t)(t1 + 1) * BB < ext ? (int64_t)(t1 + 1) * BB : ext;
+    const int PW = (int)(pend - p0);      // <= 256
+    // vertical: Vf[p0 + x][c0 + y] += sum_k U'a[src0 + k][p0 + x] R[src0 + k][c0 + y];
+    // horizontal: Hf[r0 + y][p0 + x] += sum_k U'b[src0 + k][p0 + x] Delta^T[src0 + k][r0 + y]
+    const int64_t q0 = (int64_t)(dir == 0 ? L : K) * BB;  // the source block's other side
+    const int64_t qext = dir == 0 ? n : m;
+    const int QW = (qext - q0) < BB ? (int)(qext - q0) : BB;
+    const T* pa = dir == 0 ? a.Ua : a.Ub;
+    const T* pb = dir == 0 ? a.R : a.DT;
+    const int64_t ldb = dir == 0 ? n : m;
+    T* pc = dir == 0 ? a.Vf + p0 * n + q0 : a.Hf + q0 * n + p0;
+    panel_gemm<T>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n, PW, QW, ks,
+                  dir != 0, sm);
   }
 }
 
-// Vf = Hf = 0.
+// Vf = Hf = 0 and the push queues (one counter per diagonal) = 0.
 template <typename T>
-__global__ __launch_bounds__(256) void k_init(int64_t count, T* Vf, T* Hf) {
+__global__ __launch_bounds__(256) void k_init(int64_t count, T* Vf, T* Hf, int nq, int* queue) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
        i += (int64_t)gridDim.x * 256) {
     Vf[i] = T(0);
     Hf[i] = T(0);
   }
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < nq; i += gridDim.x * 256) queue[i] = 0;
 }
 
 template <typename T>
@@ -671,6 +818,7 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   a.Hf = take();
   a.R = take();
   a.DT = take();
+  int* queue = (int*)c;  // [Mb + Nb - 1] push-task counters
   a.codes = codes;
   a.Q = Q;
   const int Mb = a.Mb, Nb = a.Nb, nD = Mb + Nb - 1;
@@ -684,19 +832,35 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   hipEvent_t* ev_round = evs + 2;      // [nD]
   hipEvent_t* ev_far = ev_round + nD;  // [nD]
   hipEvent_t ev_init = ev_far[nD];
-
+  hipStream_t sr = s, sp = s1;
   const bool pr = prof_on();
   const double es = (double)sizeof(T);
   prof_begin(KC_OTHER, s);
   k_check_scales<T><<<(unsigned)cdiv(m, 256), 256, 0, s>>>(m, scales, info);
   const int64_t ig = cdiv((int64_t)mn, 256) < 8192 ? cdiv((int64_t)mn, 256) : 8192;
-  k_init<T><<<(unsigned)ig, 256, 0, s>>>((int64_t)mn, a.Vf, a.Hf);
+  k_init<T><<<(unsigned)ig, 256, 0, s>>>((int64_t)mn, a.Vf, a.Hf, nD, queue);
   prof_end(KC_OTHER, s, 0.0, es * (2.0 * (double)mn + (double)m));
   if ((e = hipEventRecord(ev_init, s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(s1, ev_init, 0)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sp, ev_init, 0)) != hipSuccess) return e;
 
   int last_far = -1;
   const int maxt = (Mb > Nb ? Mb : Nb);
+  // push panels per (source block, direction): one near panel + far panels of four
+  const int P = 1 + (maxt + 3) / 4;
+  // The push GEMM holds more LDS than a CU can share with a rounding block, so capping
+  // its grid at (CUs - blocks of the longest diagonal) keeps CUs free for the rounding
+  // chain, whose latency-bound waves would otherwise share their SIMDs.
+  int push_grid = 0;
+  {
+    int dev = 0, ncu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) !=
+        hipSuccess)
+      return e;
+    const int maxblk = Mb < Nb ? Mb : Nb;
+    const int keep = maxblk < ncu / 2 ? maxblk : ncu / 2;
+    push_grid = ncu - keep > 1 ? ncu - keep : 1;
+  }
   std::vector<int> far_list;  // diagonals that issued pushes, increasing
   size_t fp = 0;
   int waited = -1;
@@ -709,24 +873,26 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
     while (fp < far_list.size() && far_list[fp] <= D - 2) ++fp;
     if (fp > 0 && far_list[fp - 1] != waited) {
       waited = far_list[fp - 1];
-      if ((e = hipStreamWaitEvent(s, ev_far[waited], 0)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(sr, ev_far[waited], 0)) != hipSuccess) return e;
     }
     double fl = 0.0, by = 0.0;
     if (pr) round_work(m, n, D, Mb, Nb, es, &fl, &by);
-    prof_begin(KC_ROUND, s);
-    k_round<T><<<nblk, 256, 0, s>>>(a, D);
-    prof_end(KC_ROUND, s, fl, by);
+    prof_begin(KC_ROUND, sr);
+    k_round<T><<<nblk, 256, 0, sr>>>(a, D);
+    prof_end(KC_ROUND, sr, fl, by);
     if (!push_work(m, n, D, Mb, Nb, es, &fl, &by)) continue;
-    if ((e = hipEventRecord(ev_round[D], s)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(s1, ev_round[D], 0)) != hipSuccess) return e;
-    prof_begin(KC_FAR, s1);
-    k_push<T><<<dim3(maxt, nblk, 2), 256, 0, s1>>>(a, D);
-    prof_end(KC_FAR, s1, fl, by);
-    if ((e = hipEventRecord(ev_far[D], s1)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ev_round[D], sr)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(sp, ev_round[D], 0)) != hipSuccess) return e;
+    const int ntask = nblk * 2 * P;
+    const int grid = ntask < push_grid ? ntask : push_grid;
+    prof_begin(KC_FAR, sp);
+    k_push<T><<<grid, kPushThreads, 0, sp>>>(a, D, ntask, P, queue);
+    prof_end(KC_FAR, sp, fl, by);
+    if ((e = hipEventRecord(ev_far[D], sp)) != hipSuccess) return e;
     far_list.push_back(D);
     last_far = D;
   }
-  // the call completes on the caller's stream only after the second stream drains
+  // the call completes on the caller's stream only after the push stream drains
   if (last_far >= 0 && (e = hipStreamWaitEvent(s, ev_far[last_far], 0)) != hipSuccess) return e;
   return hipGetLastError();
 }
@@ -735,7 +901,8 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
 
 size_t sweep_workspace(int64_t m, int64_t n, int dtype) {
   const size_t es = dtype == 0 ? sizeof(float) : sizeof(double);
-  return 4 * align_up((size_t)m * n * es);
+  const size_t nD = (size_t)(cdiv(m, BB) + cdiv(n, BB) - 1);
+  return 4 * align_up((size_t)m * n * es) + align_up(nD * sizeof(int));
 }
 
 hipError_t sweep_enqueue(int64_t m, int64_t n, int bits, int dtype, const void* W,
