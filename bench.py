@@ -197,7 +197,7 @@ def main():
         if name in ("near", "far"):
             return {"kernel": name, "bound": "mfma", "achieved": k["tflops"], "peak": gemm_peak,
                     "unit": "TFLOP/s", "frac": k["tflops"] / gemm_peak, "traffic": None}
-        if name in ("trailing", "trtri", "panel", "potrf"):
+        if name in ("trailing", "trtri", "panel", "potrf", "chol"):
             return {"kernel": name, "bound": "mfma", "achieved": k["tflops"],
                     "peak": PEAK["fp64_tflops"], "unit": "TFLOP/s",
                     "frac": k["tflops"] / PEAK["fp64_tflops"], "traffic": None}

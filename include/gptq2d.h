@@ -110,7 +110,7 @@ size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype);
 /*
  * Measurement hook (not part of the method): when enabled, every kernel launch of
  * the library is bracketed by a pair of HIP events on its stream and accounted to a
- * kernel class (0 round, 1 near band, 2 potrf, 3 panel, 4 trailing, 5 trtri, 6 other,
+ * kernel class (0 round, 1 near band, 2 Cholesky step, 3 panel, 4 trailing, 5 trtri, 6 other,
  * 7 far band)
  * together with the algorithmic flops and HBM bytes of that launch.  Process-wide,
  * off by default; it adds event records to the stream while on.

@@ -262,8 +262,8 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
   hipError_t e = g2d::aux_resources(2, &s1, &ev);
   if (e == hipSuccess) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) e = hipStreamWaitEvent(s1, ev[0], 0);
-  if (e == hipSuccess) e = g2d::factor_enqueue(m, dtype, A, Ua, scratch, info, 1, s);
-  if (e == hipSuccess) e = g2d::factor_enqueue(n, dtype, B, Ub, scratch_b, info, 2, s1);
+  if (e == hipSuccess)
+    e = g2d::factor_pair_enqueue(m, A, Ua, scratch, s, n, B, Ub, scratch_b, s1, dtype, info);
   if (e == hipSuccess) e = hipEventRecord(ev[1], s1);
   if (e == hipSuccess) e = hipStreamWaitEvent(s, ev[1], 0);
   if (e == hipSuccess)
@@ -311,7 +311,7 @@ int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* fl
 }
 
 const char* gptq2d_profile_class_name(int cls) {
-  static const char* names[g2d::KC_COUNT] = {"round", "near", "potrf", "panel",
+  static const char* names[g2d::KC_COUNT] = {"round", "near", "chol", "panel",
                                              "trailing", "trtri", "other", "far"};
   return (cls >= 0 && cls < g2d::KC_COUNT) ? names[cls] : "unknown";
 }

@@ -7,9 +7,10 @@
 // Adaptive Rounding", Limitations (fixed bases, factorisations computed once).
 //
 // Route (float64 throughout; MFMA f64 for the cubic parts):
-//   J A J = L L^T (lower Cholesky of the index-reversed matrix, blocked, right-looking)
-//   X = L^-1 (diagonal 64-blocks inverted in the panel kernel, the rest by recursive
-//            doubling: X21 = -X22 L21 X11)
+//   J A J = L L^T (lower Cholesky of the index-reversed matrix, blocked, right-looking,
+//            one launch per 64-wide step)
+//   X = L^-1 (diagonal 64-blocks inverted with their factorisation, the rest by
+//            recursive doubling: X21 = -X22 L21 X11)
 //   U = J X J is the upper Cholesky factor of A^-1; U'[i][j] = U[i][j] / U[i][i].
 // Diagonal-block inverses double as the panel solve: L21 = A21 (L11^-1)^T is a GEMM.
 #include <math.h>
@@ -35,17 +36,7 @@ __global__ __launch_bounds__(256) void k_reverse_sym(int64_t p, const T* __restr
   Ar[i * p + j] = (double)A[(p - 1 - b) * p + (p - 1 - a)];
 }
 
-// One diagonal 64x64 block: Cholesky, then its inverse.  Writes L into Ar (lower
-// part), X_kk = L_kk^-1 into X (zeros above the diagonal) and its transpose into DinvT.
-// Rows beyond p are padded with the identity.  256 threads, no branches in the loops.
-//  * Cholesky: thread t owns row i = t/4, columns k = 4u + t%4 (u < 16) in registers.
-//    Step j publishes the still unscaled column j (pivot included) through a double-
-//    buffered LDS column, one barrier, after which every thread applies
-//    a[i][k] -= a[i][j] a[k][j] / a[j][j] to its elements and the owners of column j
-//    scale it by 1/sqrt(a[j][j]).
-//  * Inverse: the quad of threads 4c..4c+3 forward-substitutes column c of L^-1 with
-//    the reciprocal diagonal; thread q keeps the right-hand side of rows 4u + q, and
-//    the new entry x[i][c] is broadcast inside the quad with DPP (no barrier).
+// Quad broadcast of a double: every lane of a quad receives lane `src`'s value.
 __device__ inline double quad_bcast(double v, int src) {
   // quad_perm [src, src, src, src] on both 32-bit halves (src is a literal after unrolling)
   int lo = __double2loint(v), hi = __double2hiint(v);
@@ -84,125 +75,280 @@ __device__ inline double rsq_nr(double x) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void k_potrf_diag(int64_t p, int kb, double* __restrict__ Ar,
-                                                    double* __restrict__ X,
-                                                    double* __restrict__ DinvT, int* info,
-                                                    int side_code) {
-  __shared__ double col[2][NB];
-  __shared__ double piv[NB];                // a[j][j] before scaling (for the SPD check)
-  __shared__ double rdiag[NB];              // 1 / L[j][j]
-  __shared__ double lt[NB][4][NB / 4 + 2];  // lt[c][q][u] = L[4u+q][c] (zero above diagonal)
-  const int t = threadIdx.x;
-  const int i = t >> 2, q = t & 3;
-  const int64_t r0 = (int64_t)kb * NB;
-  const int nv = (p - r0) < NB ? (int)(p - r0) : NB;
-  double a[NB / 4];
-  {
-    // all loads in flight together; rows past the matrix read as zero
-    const rsrc_t rr = make_rsrc(Ar + r0 * p + r0, ((int64_t)(nv - 1) * p + nv) * 8);
+// LDS of the diagonal-block factorisation.  Before it starts, lf and xf stage the
+// panel tiles of the previous step.
+constexpr int PD = NB + 2;
+struct BlockSmem {
+  double lf[NB][PD];  // L (zeros above the diagonal)
+  double xf[NB][PD];  // X = L^-1 (zeros above the diagonal)
+  union {
+    struct {
+      double pub[NB][4];  // the group's four columns, current values
+      double lc[NB][4];   // the group's four columns of L
+    } g;
+    double tsc[4][16][18];  // per-wave 16x16 temporaries of the inverse
+  } u;
+  double piv[NB];  // pivots before the square root (SPD check)
+};
+
+// Cholesky and inverse of one 64x64 diagonal block held in MFMA accumulator layout by
+// the four waves of the workgroup (wave w: rows 16w..16w+15, acc[t] the 16x16 tile of
+// columns 16t..16t+15; only the lower triangle is read; padding rows/columns hold the
+// identity).  Leaves L in sm.lf and X = L^-1 in sm.xf; ends with a barrier.
+//  * Cholesky, four columns at a time: the group's columns are published to LDS; lanes
+//    0..15 of every wave (one per row) factor the 4x4 diagonal block (redundantly) and
+//    solve their row's four L entries; the rank-4 update of the trailing tiles is one
+//    MFMA per tile.
+//  * Inverse by 16x16 tiles: wave t inverts diagonal tile t by forward substitution
+//    (quad c solves column c, the new entry broadcast inside the quad with DPP); the
+//    tiles below follow by distance, X_ij = -X_ii (sum_{j<=k<i} L_ik X_kj), with MFMA.
+__device__ inline void chol_inv_block(Mfma<double>::acc_t (&acc)[4], BlockSmem& sm) {
+  typedef Mfma<double>::acc_t acc_t;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, cl = lane & 15, kq = lane >> 4;
+  for (int idx = tid; idx < NB * NB; idx += 256) sm.xf[idx >> 6][idx & 63] = 0.0;
 #pragma unroll
-    for (int u = 0; u < NB / 4; ++u) a[u] = buf_load<double>(rr, (uint32_t)(i * p + 4 * u + q));
+  for (int g = 0; g < NB / 4; ++g) {
+    const int tg = g >> 2, cg = 4 * (g & 3), d0 = 4 * g;
+    if (cl >= cg && cl < cg + 4) {
 #pragma unroll
-    for (int u = 0; u < NB / 4; ++u) {
-      const int k = 4 * u + q;
-      const bool in = i < nv && k < nv;
-      a[u] = in ? (k <= i ? a[u] : 0.0) : (i == k ? 1.0 : 0.0);
+      for (int e = 0; e < 4; ++e)
+        sm.u.g.pub[16 * w + Mfma<double>::row(lane, e)][cl - cg] = acc[tg][e];
     }
-  }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int uj = j >> 2, qj = j & 3;
-    double* cj = col[j & 1];
-    if (q == qj) cj[i] = a[uj];  // column j, unscaled (rows < j hold finished L values)
     __syncthreads();
-    const double pj = cj[j];
-    const double inv = rcp_nr(pj);
-    const double rs = rsq_nr(pj);
-    const double coef = (i > j) ? cj[i] * inv : 0.0;
+    if (lane < 16) {
+      const int i = 16 * w + lane;
+      const double(*pub)[4] = sm.u.g.pub;
+      const double b00 = pub[d0][0];
+      const double b10 = pub[d0 + 1][0], b11 = pub[d0 + 1][1];
+      const double b20 = pub[d0 + 2][0], b21 = pub[d0 + 2][1], b22 = pub[d0 + 2][2];
+      const double b30 = pub[d0 + 3][0], b31 = pub[d0 + 3][1], b32 = pub[d0 + 3][2];
+      const double b33 = pub[d0 + 3][3];
+      const double q0 = b00, s0 = rsq_nr(q0);
+      const double l00 = q0 * s0, l10 = b10 * s0, l20 = b20 * s0, l30 = b30 * s0;
+      const double q1 = fma(-l10, l10, b11), s1 = rsq_nr(q1);
+      const double l11 = q1 * s1, l21 = fma(-l20, l10, b21) * s1, l31 = fma(-l30, l10, b31) * s1;
+      const double q2 = fma(-l21, l21, fma(-l20, l20, b22)), s2 = rsq_nr(q2);
+      const double l22 = q2 * s2, l32 = fma(-l31, l21, fma(-l30, l20, b32)) * s2;
+      const double q3 = fma(-l32, l32, fma(-l31, l31, fma(-l30, l30, b33))), s3 = rsq_nr(q3);
+      const double l33 = q3 * s3;
+      double x0, x1, x2, x3;
+      if (i >= d0 + 4) {
+        x0 = pub[i][0] * s0;
+        x1 = fma(-x0, l10, pub[i][1]) * s1;
+        x2 = fma(-x1, l21, fma(-x0, l20, pub[i][2])) * s2;
+        x3 = fma(-x2, l32, fma(-x1, l31, fma(-x0, l30, pub[i][3]))) * s3;
+      } else {
+        const int rr = i - d0;  // < 0 above the group: zeros
+        x0 = rr == 0 ? l00 : (rr == 1 ? l10 : (rr == 2 ? l20 : (rr == 3 ? l30 : 0.0)));
+        x1 = rr == 1 ? l11 : (rr == 2 ? l21 : (rr == 3 ? l31 : 0.0));
+        x2 = rr == 2 ? l22 : (rr == 3 ? l32 : 0.0);
+        x3 = rr == 3 ? l33 : 0.0;
+      }
+      sm.u.g.lc[i][0] = x0;
+      sm.u.g.lc[i][1] = x1;
+      sm.u.g.lc[i][2] = x2;
+      sm.u.g.lc[i][3] = x3;
+      sm.lf[i][d0] = x0;
+      sm.lf[i][d0 + 1] = x1;
+      sm.lf[i][d0 + 2] = x2;
+      sm.lf[i][d0 + 3] = x3;
+      if (i == 0) {
+        sm.piv[d0] = q0;
+        sm.piv[d0 + 1] = q1;
+        sm.piv[d0 + 2] = q2;
+        sm.piv[d0 + 3] = q3;
+      }
+    }
+    __syncthreads();
+    // rank-4 update a[i][k] -= sum_c L[i][d0+c] L[k][d0+c] of the tiles not yet finished
+    const double af = -sm.u.g.lc[16 * w + cl][kq];
 #pragma unroll
-    for (int u = 0; u < NB / 4; ++u) {
-      const int k = 4 * u + q;
-      const double ck = (k > j) ? cj[k] : 0.0;
-      a[u] = fma(-coef, ck, a[u]);
-    }
-    if (q == qj) a[uj] = (i >= j) ? a[uj] * rs : a[uj];
-    if (t == 0) {
-      piv[j] = pj;
-      rdiag[j] = rs;  // 1 / L[j][j]
-    }
+    for (int t = tg; t < 4; ++t) acc[t] = Mfma<double>::run(af, sm.u.g.lc[16 * t + cl][kq], acc[t]);
   }
-  // publish L (transposed, quad-split, zero above the diagonal) for the inverse
+  __syncthreads();  // pub/lc are dead; tsc (same storage) is used below
+  // inverse of the diagonal tile of wave w: quad c solves column c; lane q keeps the
+  // right-hand side of rows 4u + q of the tile
+  {
+    const int c = lane >> 2, q = lane & 3, o = 16 * w;
+    double rhs[4], xv[4];
 #pragma unroll
-  for (int u = 0; u < NB / 4; ++u) {
-    const int k = 4 * u + q;
-    lt[k][i & 3][i >> 2] = (k <= i) ? a[u] : 0.0;
+    for (int u = 0; u < 4; ++u) {
+      rhs[u] = (4 * u + q == c) ? 1.0 : 0.0;
+      xv[u] = 0.0;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ur = r >> 2, qr = r & 3;
+      double x = quad_bcast(rhs[ur] * rcp_nr(sm.lf[o + r][o + r]), qr);  // valid in lane qr
+      x = (r < c) ? 0.0 : x;
+      xv[ur] = (q == qr) ? x : xv[ur];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rhs[u] = fma(-sm.lf[o + 4 * u + q][o + r], x, rhs[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sm.xf[o + 4 * u + q][o + c] = xv[u];
   }
   __syncthreads();
-  if (t < 64) {  // first non-positive (or NaN) pivot, found by one wave
-    const bool bad = t < nv && !(piv[t] > 0.0);
-    const unsigned long long mask = __ballot(bad);
-    if (t == 0 && mask != 0ull) record_info(info, side_code, (int)(r0 + __ffsll((long long)mask)));
-  }
-  if (i < nv) {
+  // tiles below the diagonal, by distance d: wave w < 4 - d handles tile (w + d, w)
 #pragma unroll
-    for (int u = 0; u < NB / 4; ++u) {
-      const int k = 4 * u + q;
-      if (k <= i && k < nv) Ar[(r0 + i) * p + r0 + k] = a[u];
+  for (int d = 1; d < 4; ++d) {
+    if (w < 4 - d) {
+      const int ti = w + d, tj = w;
+      acc_t t = acc_t{0, 0, 0, 0};
+#pragma unroll
+      for (int tk = tj; tk < ti; ++tk)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          t = Mfma<double>::run(sm.lf[16 * ti + cl][16 * tk + 4 * s4 + kq],
+                                sm.xf[16 * tk + 4 * s4 + kq][16 * tj + cl], t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.u.tsc[w][Mfma<double>::row(lane, e)][cl] = t[e];
+      __asm__ volatile("" ::: "memory");  // same wave: LDS keeps program order
+      acc_t x = acc_t{0, 0, 0, 0};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        x = Mfma<double>::run(-sm.xf[16 * ti + cl][16 * ti + 4 * s4 + kq],
+                              sm.u.tsc[w][4 * s4 + kq][cl], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sm.xf[16 * ti + Mfma<double>::row(lane, e)][16 * tj + cl] = x[e];
     }
-  }
-  __syncthreads();
-  // inverse: quad c = t/4 solves column c
-  const int c = i;
-  double rhs[NB / 4], xv[NB / 4];
-#pragma unroll
-  for (int u = 0; u < NB / 4; ++u) {
-    rhs[u] = (4 * u + q == c) ? 1.0 : 0.0;
-    xv[u] = 0.0;
-  }
-#pragma unroll
-  for (int r = 0; r < NB; ++r) {
-    const int ur = r >> 2, qr = r & 3;
-    double x = quad_bcast(rhs[ur] * rdiag[r], qr);  // meaningful in lane q == qr
-    x = (r < c) ? 0.0 : x;
-    xv[ur] = (q == qr) ? x : xv[ur];
-    const double* lr = &lt[r][q][0];
-#pragma unroll
-    for (int u = 0; u < NB / 4; ++u) rhs[u] = fma(-lr[u], x, rhs[u]);
-  }
-  // X rows 4u+q, column c; DinvT[c][row] = X[row][c]
-  double* dt = DinvT + (int64_t)kb * NB * NB + (int64_t)c * NB;
-#pragma unroll
-  for (int u = 0; u < NB / 4; ++u) {
-    const int row = 4 * u + q;
-    dt[row] = xv[u];
-    if (row < nv && c < nv) X[(r0 + row) * p + r0 + c] = xv[u];
+    __syncthreads();
   }
 }
 
-// Panel solve L[i][kb] = A[i][kb] (L_kk^-1)^T for row tiles below the diagonal block.
-__global__ __launch_bounds__(256) void k_panel_solve(int64_t p, int kb, double* Ar,
-                                                     const double* __restrict__ DinvT) {
-  __shared__ TileSmem<double> sm;
-  const int64_t r0 = (int64_t)(kb + 1 + blockIdx.x) * NB;
-  const int64_t c0 = (int64_t)kb * NB;
-  const int M = (p - r0) < NB ? (int)(p - r0) : NB;
-  const int K = (p - c0) < NB ? (int)(p - c0) : NB;
-  double* tile = Ar + r0 * p + c0;
-  tile_gemm<double, false, false>(tile, p, DinvT + (int64_t)kb * NB * NB, NB, tile, p, M, K, 0, K,
-                                  1.0, 0.0, sm);
-}
-
-// Trailing update of the lower triangle: Ar[i][j] -= L[i][kb] L[j][kb]^T, kb < j <= i.
-__global__ __launch_bounds__(256) void k_trailing(int64_t p, int kb, double* Ar) {
-  __shared__ TileSmem<double> sm;
-  const int i = kb + 1 + blockIdx.y, j = kb + 1 + blockIdx.x;
-  if (j > i) return;
-  const int64_t r0 = (int64_t)i * NB, cj = (int64_t)j * NB, ck = (int64_t)kb * NB;
-  const int M = (p - r0) < NB ? (int)(p - r0) : NB;
-  const int N = (p - cj) < NB ? (int)(p - cj) : NB;
-  const int K = (p - ck) < NB ? (int)(p - ck) : NB;
-  tile_gemm<double, false, true>(Ar + r0 * p + ck, p, Ar + cj * p + ck, p, Ar + r0 * p + cj, p, M,
-                                 N, 0, K, -1.0, 1.0, sm);
+// One step s of the blocked right-looking Cholesky of the reversed matrix, in one launch.
+//  * Workgroups 0 .. nblk-s-1 ("critical"): workgroup c handles row tile i = s + c of block
+//    column s.  Each subtracts the previous panel's contribution from the diagonal tile
+//    (s, s) and factors it (every critical workgroup does this identically, so none waits
+//    for another); workgroup 0 writes L_ss and X_ss = L_ss^-1, the others update their tile
+//    (i, s) with the previous panel and solve L_is = A_is X_ss^T.
+//  * The remaining workgroups ("bulk") apply the previous panel to the trailing tiles
+//    (i, j), s < j <= i: A_ij -= L_i,s-1 L_j,s-1^T.
+// So the panel chain and the bulk trailing update of the previous step share a launch.
+__global__ __launch_bounds__(256, 2) void k_chol_step(int64_t p, int s, double* __restrict__ Ar,
+                                                      double* __restrict__ X, int* info,
+                                                      int side_code) {
+  typedef Mfma<double>::acc_t acc_t;
+  __shared__ union {
+    BlockSmem b;
+    TileSmem<double> t;
+  } sh;
+  const int nblk = (int)((p + NB - 1) / NB);
+  const int crit = nblk - s;
+  if ((int)blockIdx.x >= crit) {
+    const int rest = nblk - s - 1, idx = (int)blockIdx.x - crit;
+    const int bi = idx / rest, bj = idx % rest;
+    if (bj > bi) return;
+    const int i = s + 1 + bi, j = s + 1 + bj;
+    const int64_t ri = (int64_t)i * NB, cj = (int64_t)j * NB, ck = (int64_t)(s - 1) * NB;
+    const int M = (p - ri) < NB ? (int)(p - ri) : NB;
+    const int N = (p - cj) < NB ? (int)(p - cj) : NB;
+    tile_gemm<double, false, true>(Ar + ri * p + ck, p, Ar + cj * p + ck, p, Ar + ri * p + cj, p,
+                                   M, N, 0, NB, -1.0, 1.0, sh.t);
+    return;
+  }
+  BlockSmem& sm = sh.b;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, cl = lane & 15, kq = lane >> 4;
+  const int i = s + (int)blockIdx.x;
+  const int64_t r0 = (int64_t)s * NB, ri = (int64_t)i * NB;
+  const int nv = (p - r0) < NB ? (int)(p - r0) : NB;  // rows/columns of block s
+  const int mi = (p - ri) < NB ? (int)(p - ri) : NB;  // rows of tile i
+  const bool diag = i == s;
+  acc_t acc[4], pt[4];
+  {
+    // all loads in flight together; entries outside the matrix read as zero.  The
+    // previous panel's tiles (s, s-1) and (i, s-1) are staged in lf / xf.
+    const rsrc_t rd = make_rsrc(Ar + r0 * p + r0, ((int64_t)(nv - 1) * p + nv) * 8);
+    const rsrc_t rp = make_rsrc(Ar + ri * p + r0, ((int64_t)(mi - 1) * p + nv) * 8);
+    double v[4][4], u[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + Mfma<double>::row(lane, e), k = 16 * t + cl;
+        v[t][e] = buf_load<double>(rd, (uint32_t)(r * p + k));
+        u[t][e] = diag ? 0.0 : buf_load<double>(rp, (uint32_t)(r * p + k));
+      }
+    if (s > 0) {
+      const int64_t cp = (int64_t)(s - 1) * NB;  // block column s-1 is full width
+      const rsrc_t rs = make_rsrc(Ar + r0 * p + cp, ((int64_t)(nv - 1) * p + NB) * 8);
+      const rsrc_t rq = make_rsrc(Ar + ri * p + cp, ((int64_t)(mi - 1) * p + NB) * 8);
+      double a1[16], a2[16];
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int idx = tid + 256 * it, r = idx >> 6, k = idx & 63;
+        a1[it] = buf_load<double>(rs, (uint32_t)(r * p + k));
+        a2[it] = diag ? 0.0 : buf_load<double>(rq, (uint32_t)(r * p + k));
+      }
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int idx = tid + 256 * it, r = idx >> 6, k = idx & 63;
+        sm.lf[r][k] = a1[it];
+        sm.xf[r][k] = a2[it];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + Mfma<double>::row(lane, e), k = 16 * t + cl;
+        acc[t][e] = (r < nv && k < nv) ? (k <= r ? v[t][e] : 0.0) : (r == k ? 1.0 : 0.0);
+        pt[t][e] = u[t][e];
+      }
+  }
+  if (s > 0) {
+    __syncthreads();
+    // A_ss -= L_s,s-1 L_s,s-1^T and A_is -= L_i,s-1 L_s,s-1^T (rows of L past the matrix
+    // are zero, so the identity padding stays)
+#pragma unroll
+    for (int ks = 0; ks < NB / 4; ++ks) {
+      const double as = -sm.lf[16 * w + cl][4 * ks + kq];
+      const double ai = -sm.xf[16 * w + cl][4 * ks + kq];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const double b = sm.lf[16 * t + cl][4 * ks + kq];
+        acc[t] = Mfma<double>::run(as, b, acc[t]);
+        if (!diag) pt[t] = Mfma<double>::run(ai, b, pt[t]);
+      }
+    }
+    __syncthreads();  // the staging is consumed before the factorisation reuses lf / xf
+  }
+  chol_inv_block(acc, sm);
+  if (diag) {
+    if (tid < 64) {  // first non-positive (or NaN) pivot, found by one wave
+      const bool bad = tid < nv && !(sm.piv[tid] > 0.0);
+      const unsigned long long mask = __ballot(bad);
+      if (tid == 0 && mask != 0ull)
+        record_info(info, side_code, (int)(r0 + __ffsll((long long)mask)));
+    }
+    for (int idx = tid; idx < NB * NB; idx += 256) {
+      const int r = idx >> 6, k = idx & 63;
+      if (r < nv && k < nv) {
+        if (k <= r) Ar[(r0 + r) * p + r0 + k] = sm.lf[r][k];
+        X[(r0 + r) * p + r0 + k] = sm.xf[r][k];
+      }
+    }
+    return;
+  }
+  // L_is = A_is X_ss^T: A_is goes through lf (free after the factorisation)
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.lf[16 * w + Mfma<double>::row(lane, e)][16 * t + cl] = pt[t][e];
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    acc_t o = acc_t{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < NB / 4; ++ks)
+      o = Mfma<double>::run(sm.lf[16 * w + cl][4 * ks + kq], sm.xf[16 * t + cl][4 * ks + kq], o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + Mfma<double>::row(lane, e), k = 16 * t + cl;
+      if (r < mi && k < nv) Ar[(ri + r) * p + r0 + k] = o[e];
+    }
+  }
 }
 
 // Recursive doubling, step 1: T = L21 X11 for every pair of h-blocks (group z).
@@ -258,7 +404,6 @@ __global__ __launch_bounds__(256) void k_finalize(int64_t p, const double* __res
 struct FactorWs {
   double* Ar;
   double* X;
-  double* DinvT;
   double* Tb;
   int64_t ldt;
 };
@@ -273,14 +418,11 @@ int64_t trtri_ldt(int64_t p) {
 FactorWs carve(int64_t p, void* ws) {
   FactorWs f;
   char* c = (char*)ws;
-  const int64_t nblk = cdiv(p, NB);
   f.ldt = trtri_ldt(p);
   f.Ar = (double*)c;
   c += align_up((size_t)p * p * sizeof(double));
   f.X = (double*)c;
   c += align_up((size_t)p * p * sizeof(double));
-  f.DinvT = (double*)c;
-  c += align_up((size_t)nblk * NB * NB * sizeof(double));
   f.Tb = (double*)c;
   return f;
 }
@@ -288,11 +430,8 @@ FactorWs carve(int64_t p, void* ws) {
 }  // namespace
 
 size_t factor_workspace(int64_t p) {
-  const int64_t nblk = cdiv(p, NB);
   const int64_t ldt = trtri_ldt(p);
-  return 2 * align_up((size_t)p * p * sizeof(double)) +
-         align_up((size_t)nblk * NB * NB * sizeof(double)) +
-         align_up((size_t)p * ldt * sizeof(double));
+  return 2 * align_up((size_t)p * p * sizeof(double)) + align_up((size_t)p * ldt * sizeof(double));
 }
 
 // Dense GEMM flops of one launch (only evaluated while the measurement hook is on).
@@ -328,52 +467,105 @@ void trtri_flops(int64_t p, int64_t h, double* f1, double* f2) {
   }
 }
 
-hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws, int* info,
-                          int side_code, hipStream_t s) {
-  FactorWs f = carve(p, ws);
-  const int64_t nblk = cdiv(p, NB);
+namespace {
+
+// The launches of one factorisation, in order: reversal, one per Cholesky step, one per
+// doubling level of the inverse (two kernels), finalisation.
+struct FactorPlan {
+  int64_t p;
+  int dtype;
+  const void* A;
+  void* U;
+  FactorWs f;
+  int* info;
+  int side_code;
+  hipStream_t s;
+  int nblk, nlev;
+  int stages() const { return 1 + nblk + nlev + 1; }
+};
+
+FactorPlan plan(int64_t p, int dtype, const void* A, void* U, void* ws, int* info, int side_code,
+                hipStream_t s) {
+  FactorPlan q{p, dtype, A, U, carve(p, ws), info, side_code, s, (int)cdiv(p, NB), 0};
+  for (int64_t h = NB; h < p; h *= 2) ++q.nlev;
+  return q;
+}
+
+void stage(const FactorPlan& q, int idx) {
+  const int64_t p = q.p;
   const bool pr = prof_on();
-  const double es = dtype == 0 ? 4.0 : 8.0, pp = (double)p * (double)p;
-  dim3 eg((unsigned)cdiv(p, 64), (unsigned)cdiv(p, 4));
-  prof_begin(KC_OTHER, s);
-  if (dtype == 0)
-    k_reverse_sym<float><<<eg, 256, 0, s>>>(p, (const float*)A, f.Ar);
-  else
-    k_reverse_sym<double><<<eg, 256, 0, s>>>(p, (const double*)A, f.Ar);
-  prof_end(KC_OTHER, s, 0.0, pp * (es + 8.0));
-  for (int kb = 0; kb < nblk; ++kb) {
-    const double nv = (double)((p - kb * NB) < NB ? (p - kb * NB) : NB);
-    prof_begin(KC_POTRF, s);
-    k_potrf_diag<<<1, 256, 0, s>>>(p, kb, f.Ar, f.X, f.DinvT, info, side_code);
-    prof_end(KC_POTRF, s, 2.0 / 3.0 * nv * nv * nv, 8.0 * (nv * nv * 2.5 + NB * NB));
-    const int rest = (int)(nblk - kb - 1);
-    if (rest > 0) {
-      const double rows = (double)(p - (int64_t)(kb + 1) * NB);
-      prof_begin(KC_PANEL, s);
-      k_panel_solve<<<rest, 256, 0, s>>>(p, kb, f.Ar, f.DinvT);
-      prof_end(KC_PANEL, s, 2.0 * rows * nv * nv, 8.0 * (2.0 * rows * nv + nv * nv));
-      prof_begin(KC_TRAILING, s);
-      k_trailing<<<dim3(rest, rest), 256, 0, s>>>(p, kb, f.Ar);
-      prof_end(KC_TRAILING, s, pr ? trailing_flops(p, kb) : 0.0,
-               8.0 * (rows * (rows + NB) + rows * nv));
-    }
+  const double es = q.dtype == 0 ? 4.0 : 8.0, pp = (double)p * (double)p;
+  hipStream_t s = q.s;
+  const FactorWs& f = q.f;
+  const dim3 eg((unsigned)cdiv(p, 64), (unsigned)cdiv(p, 4));
+  if (idx == 0) {
+    prof_begin(KC_OTHER, s);
+    if (q.dtype == 0)
+      k_reverse_sym<float><<<eg, 256, 0, s>>>(p, (const float*)q.A, f.Ar);
+    else
+      k_reverse_sym<double><<<eg, 256, 0, s>>>(p, (const double*)q.A, f.Ar);
+    prof_end(KC_OTHER, s, 0.0, pp * (es + 8.0));
+    return;
   }
-  for (int64_t h = NB; h < p; h *= 2) {
+  if (idx <= q.nblk) {
+    const int st = idx - 1;
+    const int crit = q.nblk - st, rest = q.nblk - st - 1;
+    const unsigned grid = (unsigned)(crit + (st > 0 ? rest * rest : 0));
+    double fl = 0.0, by = 0.0;
+    if (pr) {
+      const double nv = (double)((p - st * NB) < NB ? (p - st * NB) : NB);
+      const double rows = (double)(p - (int64_t)st * NB) - nv;
+      fl = 2.0 / 3.0 * nv * nv * nv + 2.0 * rows * nv * nv +
+           (st > 0 ? trailing_flops(p, st - 1) : 0.0);
+      const double trail = st > 0 ? (rows + nv) * (rows + nv + NB) / 2.0 : 0.0;
+      by = 8.0 * (3.0 * (rows + nv) * NB + 3.0 * trail);
+    }
+    prof_begin(KC_POTRF, s);
+    k_chol_step<<<grid, 256, 0, s>>>(p, st, f.Ar, f.X, q.info, q.side_code);
+    prof_end(KC_POTRF, s, fl, by);
+    return;
+  }
+  if (idx <= q.nblk + q.nlev) {
+    const int64_t h = (int64_t)NB << (idx - q.nblk - 1);
     const int64_t groups = cdiv(p, 2 * h);
-    dim3 g((unsigned)cdiv(h, NB), (unsigned)cdiv(h, NB), (unsigned)groups);
+    const dim3 g((unsigned)cdiv(h, NB), (unsigned)cdiv(h, NB), (unsigned)groups);
     double f1 = 0.0, f2 = 0.0;
     if (pr) trtri_flops(p, h, &f1, &f2);
     prof_begin(KC_TRTRI, s);
     k_trtri_step1<<<g, 256, 0, s>>>(p, h, f.Ar, f.X, f.Tb, f.ldt);
     k_trtri_step2<<<g, 256, 0, s>>>(p, h, f.X, f.Tb, f.ldt);
     prof_end(KC_TRTRI, s, f1 + f2, 8.0 * 4.0 * (double)h * (double)p);
+    return;
   }
   prof_begin(KC_OTHER, s);
-  if (dtype == 0)
-    k_finalize<float><<<eg, 256, 0, s>>>(p, f.X, (float*)U);
+  if (q.dtype == 0)
+    k_finalize<float><<<eg, 256, 0, s>>>(p, f.X, (float*)q.U);
   else
-    k_finalize<double><<<eg, 256, 0, s>>>(p, f.X, (double*)U);
+    k_finalize<double><<<eg, 256, 0, s>>>(p, f.X, (double*)q.U);
   prof_end(KC_OTHER, s, 0.0, pp * (8.0 / 2.0 + es));
+}
+
+}  // namespace
+
+hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws, int* info,
+                          int side_code, hipStream_t s) {
+  const FactorPlan q = plan(p, dtype, A, U, ws, info, side_code, s);
+  for (int i = 0; i < q.stages(); ++i) stage(q, i);
+  return hipGetLastError();
+}
+
+hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, hipStream_t sa,
+                               int64_t n, const void* B, void* Ub, void* ws_b, hipStream_t sb,
+                               int dtype, int* info) {
+  // launches alternate between the two chains so that both streams have work queued
+  // from the start and the two factorisations overlap on the device
+  const FactorPlan qa = plan(m, dtype, A, Ua, ws_a, info, 1, sa);
+  const FactorPlan qb = plan(n, dtype, B, Ub, ws_b, info, 2, sb);
+  const int na = qa.stages(), nb = qb.stages();
+  for (int i = 0; i < (na > nb ? na : nb); ++i) {
+    if (i < na) stage(qa, i);
+    if (i < nb) stage(qb, i);
+  }
   return hipGetLastError();
 }
 

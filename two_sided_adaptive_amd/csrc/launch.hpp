@@ -22,6 +22,11 @@ hipError_t aux_resources(size_t nevents, hipStream_t* aux, hipEvent_t** events);
 size_t factor_workspace(int64_t p);
 hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws, int* info,
                           int side_code, hipStream_t s);
+// Both factors at once: A (m x m) on stream sa and B (n x n) on stream sb, with their
+// launches interleaved on the host; info codes 1 for A and 2 for B.
+hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, hipStream_t sa,
+                               int64_t n, const void* B, void* Ub, void* ws_b, hipStream_t sb,
+                               int dtype, int* info);
 
 // Sweep stage (sweep.hip): codes/Q from W, U'_a, U'_b, scales (all dtype).
 size_t sweep_workspace(int64_t m, int64_t n, int dtype);

@@ -11,7 +11,7 @@ namespace g2d {
 enum KernelClass : int {
   KC_ROUND = 0,     // anti-diagonal rounding of one block diagonal
   KC_BAND = 1,      // near band feedback GEMMs of one block diagonal
-  KC_POTRF = 2,     // diagonal-block Cholesky + inverse
+  KC_POTRF = 2,     // one Cholesky step: diagonal block + inverse, panel, trailing
   KC_PANEL = 3,     // panel solve GEMM
   KC_TRAILING = 4,  // trailing-update GEMM of the Cholesky
   KC_TRTRI = 5,     // triangular-inverse doubling GEMMs

@@ -507,38 +507,44 @@ struct PushKc<double> {
 // LDS row strides (elements) of the staged operands: a multiple of 16 plus 16, so the
 // four k-rows read by one MFMA operand load start 32 dwords (f64) or 16 dwords (f32)
 // apart and fall in different banks.
-constexpr int kPadWide = 256 + 16;  // 256-wide operand
-constexpr int kPadNarrow = 64 + 16;  // 64-wide operand
+constexpr int kPanel = 2;                   // target blocks per push task
+constexpr int kPadWide = kPanel * 64 + 16;  // panel-wide operand
+constexpr int kPadNarrow = 64 + 16;         // 64-wide operand
 constexpr int kPushThreads = 512;
+constexpr int kNearPanels = (3 + kPanel - 1) / kPanel;  // near targets: at most three
 template <typename T>
 struct PushSmem {
   static constexpr int KC = PushKc<T>::v;
-  T buf[KC * (kPadWide + kPadNarrow)];  // A rows, then B rows
+  // A rows, then B rows; also the 64 x 130 transpose stage of the epilogue
+  static constexpr int kElems = KC * (kPadWide + kPadNarrow) > 64 * 130 ? KC * (kPadWide + kPadNarrow) : 64 * 130;
+  T buf[kElems];
   int task;
 };
 
-// G[x][y] = sum_{k<K} A[k*lda + x] B[k*ldb + y] for x < M <= 256, y < N <= 64, both
-// operands k-major, added into C: C[x*ldc + y] += G[x][y], or with `trans`
+// G[x][y] = sum_{k<K} A[k*lda + x] B[k*ldb + y] for x < M <= BM, y < N <= 64 (BM = 128
+// or 256), both operands k-major, added into C: C[x*ldc + y] += G[x][y], or with `trans`
 // C[y*ldc + x] += G[x][y].  One workgroup of eight waves, two per SIMD; wave w owns rows
-// x in [32w, 32w+32) as 2x4 MFMA tiles.  Operands are staged through LDS KC k-rows at a
+// x in [w BM/8, (w+1) BM/8) as (BM/128) x 4 MFMA tiles.  Operands are staged through LDS KC k-rows at a
 // time, with the next chunk's global loads in flight in registers while the current
 // chunk is multiplied.  k-rows past K read as zero (exact buffer ranges); rows or
 // columns past M, N read neighbouring finite data that only reaches outputs that are
 // never stored.  The transposed update goes through LDS so that its stores are
 // coalesced along x.
-template <typename T>
+template <typename T, int BM>
 __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t ldb, T* C,
                                   int64_t ldc, int M, int N, int K, bool trans,
                                   PushSmem<T>& sm) {
   typedef typename Mfma<T>::acc_t acc_t;
-  constexpr int BM = 256, BN = 64;
+  constexpr int BN = 64;
+  static_assert(BM == 128 || BM == 256, "panel width");
   constexpr int KC = PushKc<T>::v;
-  constexpr int SA = kPadWide, SB = kPadNarrow;
+  constexpr int SA = BM + 16, SB = kPadNarrow;
+  static_assert(SA <= kPadWide, "stage layout");
   constexpr int TH = kPushThreads;
   constexpr int NA = KC * BM / TH, NB = KC * BN / TH;  // staged elements per thread
-  constexpr int TM = 2, TN = 4;
+  constexpr int TM = BM / 128, TN = 4;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wi0 = 32 * w;
+  const int wi0 = (BM / 8) * w;
   const int kq = lane >> 4, cl = lane & 15;
   const int64_t es = sizeof(T);
   const rsrc_t ra = make_rsrc(A, ((int64_t)(K - 1) * lda + M) * es);
@@ -620,13 +626,14 @@ __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t l
     }
     return;
   }
-  // transposed: two halves of 128 x-values; the owners write G^T into LDS (pitch 130),
-  // then every thread updates whole C rows
+  // transposed: halves of 128 x-values; the owners write G^T into LDS (pitch 130), then
+  // every thread updates whole C rows
   constexpr int PT = 128 + 2;
+  static_assert(64 * PT <= PushSmem<T>::kElems, "transpose stage");
   const rsrc_t rc = make_rsrc(C, ((int64_t)(N - 1) * ldc + M) * es);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if ((w >> 2) == h) {
+  for (int h = 0; h < BM / 128; ++h) {
+    if (wi0 / 128 == h) {
 #pragma unroll
       for (int x = 0; x < TM; ++x)
 #pragma unroll
@@ -652,11 +659,11 @@ __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t l
 // Band pushes of the blocks on diagonal D that later diagonals do not pull themselves.
 // Vertical (into Vf) from block (K, L) to row blocks t >= K+2 of column L, horizontal
 // (into Hf) from (K, L) to column blocks t >= L+2 of row K.  Targets up to the first
-// block of the next outer block take the 64-deep panel of (K, L) (one "near" panel of at
-// most three targets); beyond that, a block that closes an outer block pushes the whole
-// outer block, 256 deep, in panels of four targets.  Workgroups take tasks (panel,
-// direction, source block) from a queue, far panels first; each target tile is written
-// by one task, so the order of tasks does not matter for the result.
+// block of the next outer block take the 64-deep panel of (K, L) ("near": at most three
+// targets); beyond that, a block that closes an outer block pushes the whole outer
+// block, 256 deep.  Tasks cover kPanel target blocks each.  Workgroups take tasks
+// (panel, direction, source block) from a queue, far panels first; each target tile is
+// written by one task, so the order of tasks does not matter for the result.
 template <typename T>
 __global__ __launch_bounds__(kPushThreads) void k_push(SweepArgs<T> a, int D, int ntask, int P,
                                                        int* queue) {
@@ -678,22 +685,23 @@ __global__ __launch_bounds__(kPushThreads) void k_push(SweepArgs<T> a, int D, in
     const int64_t ext = dir == 0 ? m : n;
     int t0, t1, ks;
     int64_t src0;
-    if (panel == 0) {
-      t0 = own + 2;
-      t1 = first_next < nt - 1 ? first_next : nt - 1;
+    if (panel < kNearPanels) {
+      const int nlast = first_next < nt - 1 ? first_next : nt - 1;
+      t0 = own + 2 + kPanel * panel;
+      t1 = t0 + kPanel - 1 < nlast ? t0 + kPanel - 1 : nlast;
       src0 = (int64_t)own * BB;
       ks = (ext - src0) < BB ? (int)(ext - src0) : BB;
     } else {
       if (own % GOUT != GOUT - 1) continue;
-      t0 = first_next + 1 + 4 * (panel - 1);
-      t1 = t0 + 3 < nt - 1 ? t0 + 3 : nt - 1;
+      t0 = first_next + 1 + kPanel * (panel - kNearPanels);
+      t1 = t0 + kPanel - 1 < nt - 1 ? t0 + kPanel - 1 : nt - 1;
       src0 = (int64_t)(own - (GOUT - 1)) * BB;
       ks = GOUT * BB;
     }
     if (t0 > t1) continue;
     const int64_t p0 = (int64_t)t0 * BB;  // first pushed row (dir 0) or column (dir 1)
     const int64_t pend = (int64_t)(t1 + 1) * BB < ext ? (int64_t)(t1 + 1) * BB : ext;
-    const int PW = (int)(pend - p0);      // <= 256
+    const int PW = (int)(pend - p0);      // <= 64 kPanel
     // vertical: Vf[p0 + x][c0 + y] += sum_k U'a[src0 + k][p0 + x] R[src0 + k][c0 + y];
     // horizontal: Hf[r0 + y][p0 + x] += sum_k U'b[src0 + k][p0 + x] Delta^T[src0 + k][r0 + y]
     const int64_t q0 = (int64_t)(dir == 0 ? L : K) * BB;  // the source block's other side
@@ -703,8 +711,8 @@ __global__ __launch_bounds__(kPushThreads) void k_push(SweepArgs<T> a, int D, in
     const T* pb = dir == 0 ? a.R : a.DT;
     const int64_t ldb = dir == 0 ? n : m;
     T* pc = dir == 0 ? a.Vf + p0 * n + q0 : a.Hf + q0 * n + p0;
-    panel_gemm<T>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n, PW, QW, ks,
-                  dir != 0, sm);
+    panel_gemm<T, 64 * kPanel>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n, PW,
+                               QW, ks, dir != 0, sm);
   }
 }
 
@@ -845,8 +853,8 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
 
   int last_far = -1;
   const int maxt = (Mb > Nb ? Mb : Nb);
-  // push panels per (source block, direction): one near panel + far panels of four
-  const int P = 1 + (maxt + 3) / 4;
+  // push panels per (source block, direction): near panels + far panels of kPanel blocks
+  const int P = kNearPanels + (maxt + kPanel - 1) / kPanel;
   // The push GEMM holds more LDS than a CU can share with a rounding block, so capping
   // its grid at (CUs - blocks of the longest diagonal) keeps CUs free for the rounding
   // chain, whose latency-bound waves would otherwise share their SIMDs.
