@@ -1,5 +1,5 @@
 // Sweep stage for gfx950: anti-diagonal two-sided adaptive rounding with
-// separable band feedback.
+// separable band feedback, as one persistent kernel.
 //
 // Page reference: arxivlens page "GPTQ-2D: Cubic-Time Two-Sided Adaptive Rounding",
 // Results (entries of one anti-diagonal are independent and are rounded together;
@@ -14,20 +14,30 @@
 // entries above it in its column and left of it in its row, so every anti-diagonal
 // is an antichain.
 //
-// Blocking (64 x 64 blocks; outer blocks of 4 x 4 blocks):
-//   * k_round rounds all blocks of one block anti-diagonal D.  It first pulls the band
-//     feedback of the two neighbours just finished on D-1 (block above: Ua'^T R, 64
-//     deep; block to the left: Delta Ub', 64 deep) with MFMA, adds what k_push has
-//     accumulated in Vf/Hf, and then rounds the block: the four waves own 16-row
-//     micro-rows and walk 16x16 micro-tiles along micro anti-diagonals; feedback
-//     between micro-tiles is an MFMA product from LDS, feedback inside a micro-tile is
-//     applied entry by entry along its 31 anti-diagonal steps.
-//   * k_push (second stream, off the critical path) pushes everything else into Vf
-//     (vertical, -Ua'^T R) and Hf (horizontal, +Delta Ub'): 64 deep from a block to
-//     the blocks two or more past it up to the first block of the next outer block,
-//     and, when a block closes an outer block, 256 deep from the whole outer block to
-//     every block beyond.  All those targets lie two or more block diagonals ahead,
-//     which is the slack that lets it overlap the rounding.
+// Work decomposition (bands of 64 rows, 16 x 16 micro-tiles, 64-wide column blocks,
+// outer blocks of four bands / blocks):
+//   * A band worker (one workgroup, four waves) owns a band and walks its micro-columns
+//     left to right.  Wave w owns micro-row w; at phase p it rounds micro-tile
+//     (w, p - w), so the four waves form a skewed pipeline that follows the
+//     anti-diagonals of the band.  The feedback a micro-tile needs is
+//       - from its own rows and columns: applied entry by entry along its 31
+//         anti-diagonal steps;
+//       - from the band's earlier micro-rows (same micro-column) and from the previous
+//         band (64 rows): MFMA products, the latter waiting on a per-band progress
+//         counter of the band above;
+//       - from the band's own micro-columns in the current and the previous column
+//         block: MFMA products from the band's Delta history in LDS;
+//       - from everything further away: the accumulated buffers Vf (vertical) and Hf
+//         (horizontal), filled by GEMM workers.
+//     Consecutive bands therefore run one micro-column phase apart per wave: the
+//     wavefront of the whole matrix advances one micro-tile anti-diagonal at a time.
+//   * GEMM workers take band-update tasks from a queue that band workers fill when
+//     they complete a 64 x 64 block: 64 deep from one band (block) to the targets up to
+//     the first block of the next outer block, and, when the block closes an outer
+//     block, 256 deep from the whole outer block to every target beyond.  The
+//     contributions to one target tile are applied in the order of their sources, so
+//     the result is deterministic.
+// Every wait is bounded; a timeout aborts the sweep and reports info[0] = 4.
 #include <math.h>
 
 #include <mutex>
@@ -40,62 +50,185 @@
 namespace g2d {
 namespace {
 
-constexpr int BB = 64;   // block edge
-constexpr int MU = 16;   // micro-tile edge
-constexpr int GOUT = 4;  // blocks per outer block edge (outer block = 256)
+constexpr int BB = 64;      // band height = block edge
+constexpr int MU = 16;      // micro-tile edge
+constexpr int GOUT = 4;     // bands (blocks) per outer band (block)
+constexpr int FAR_OFF = 1;  // far pushes of outer band O reach targets >= GOUT (O + 1) + FAR_OFF
+constexpr int kPanel = 2;   // target blocks per GEMM task
+constexpr int kThreads = 256;
+constexpr int kSpinLimit = 1 << 22;
+
+// control words at the start of the sync area
+enum Ctl : int { kBandCtr = 0, kHead = 1, kTail = 2, kAbort = 3, kTicket = 4, kCtlWords = 8 };
+
+// Cache policy of loads and stores that other workgroups of the same launch produce or
+// consume: device scope (sc1), so they bypass the non-coherent caches.
+constexpr int kDev = 16;
 
 template <typename T>
 struct SweepArgs {
   int64_t m, n;
-  int Mb, Nb, lo, hi, bits;
+  int Mb, Nb, Nj, lo, hi, bits;
+  int total;  // band-update tasks in the whole sweep
+  int nbw;    // band workers
   const T* Ua;
   const T* Ub;
   const T* s;
   const T* W;
-  T* Vf;   // vertical feedback pushed by k_push (subtracted from W)
-  T* Hf;   // horizontal feedback pushed by k_push
+  T* Vf;   // vertical feedback pushed by GEMM workers (subtracted from W)
+  T* Hf;   // horizontal feedback pushed by GEMM workers
   T* R;    // vertical residual, row-major m x n
   T* DT;   // Delta transposed, n x m
   int8_t* codes;
   T* Q;
+  int* info;
+  int* ctl;                  // kCtlWords control words
+  int* rdone;                // [Mb] micro-columns of each band whose R is stored
+  int* vcnt;                 // [Mb * Nb] contributions applied to Vf, per 64 x 64 tile
+  int* hcnt;                 // [Mb * Nb] contributions applied to Hf, per tile
+  unsigned long long* qd;    // [total] task descriptors (0 = not yet published)
 };
 
-// Row strides keep 4-element groups 16-byte aligned for vector LDS reads.
-template <typename T>
-struct Pad;
-template <>
-struct Pad<float> {
-  static constexpr int v = 68;
-};
-template <>
-struct Pad<double> {
-  static constexpr int v = 66;
-};
+// ---------------------------------------------------------------------------
+// push rules (host and device)
+// ---------------------------------------------------------------------------
+// Source index `own` (a band for vertical pushes, a column block for horizontal ones)
+// pushes 64 deep to targets [own + 2, GOUT (own / GOUT) + GOUT - 1 + FAR_OFF]; the last
+// band of an outer band pushes the whole outer band, 256 deep, to every target from
+// GOUT (own / GOUT + 1) + FAR_OFF on.  Target T thus receives, in source order, the far
+// pushes of outer bands 0 .. nfar(T) - 1 and then the near pushes of the bands
+// GOUT nfar(T) .. T - 2; band T - 1 is applied by the band worker itself.
+__host__ __device__ inline int nfar(int T) {
+  return T >= GOUT + FAR_OFF ? (T - GOUT - FAR_OFF) / GOUT + 1 : 0;
+}
+__host__ __device__ inline int expected_pushes(int T) {
+  return T >= 2 ? T - 1 - (GOUT - 1) * nfar(T) : 0;
+}
+__host__ __device__ inline int push_seq(int T, int own, bool far) {
+  return far ? own / GOUT : nfar(T) + (own - GOUT * nfar(T));
+}
+__host__ __device__ inline void near_range(int own, int nt, int* t0, int* t1) {
+  *t0 = own + 2;
+  const int e = GOUT * (own / GOUT) + GOUT - 1 + FAR_OFF;
+  *t1 = e < nt - 1 ? e : nt - 1;
+}
+__host__ __device__ inline void far_range(int own, int nt, int* t0, int* t1) {
+  if (own % GOUT != GOUT - 1) {
+    *t0 = 1;
+    *t1 = 0;
+    return;
+  }
+  *t0 = GOUT * (own / GOUT + 1) + FAR_OFF;
+  *t1 = nt - 1;
+}
+__host__ __device__ inline int npanels(int t0, int t1) {
+  return t1 >= t0 ? (t1 - t0) / kPanel + 1 : 0;
+}
+__host__ __device__ inline int block_task_count(int K, int L, int Mb, int Nb) {
+  int t0, t1, c = 0;
+  near_range(K, Mb, &t0, &t1);
+  c += npanels(t0, t1);
+  near_range(L, Nb, &t0, &t1);
+  c += npanels(t0, t1);
+  far_range(K, Mb, &t0, &t1);
+  c += npanels(t0, t1);
+  far_range(L, Nb, &t0, &t1);
+  c += npanels(t0, t1);
+  return c;
+}
 
-template <typename T>
-struct RoundSmem {
-  static constexpr int P = Pad<T>::v;
-  T ua[BB][P];           // diagonal block of U'a, row-major, strictly upper
-  T ubT[BB][P];          // diagonal block of U'b, transposed: ubT[c][k] = U'b[k][c]
-  T rT[BB][P];           // R of this block, transposed: rT[c][i] = R[i][c]
-  T dd[BB][P];           // Delta of this block, row-major
-  T g0s[4][MU][MU];      // per wave, skewed: g0s[r][sl] = (W - G outside)[r][(sl - r) % 16]
-  T h0s[4][MU][MU];      // per wave, skewed: H pushed from outside; scratch during a sweep
-  T sc[BB];              // scales
-  T rs[BB];              // fl(1 / scale)
-  T sup[BB][2];          // sup[c] = (U'b[c-2][c], U'b[c-1][c]) inside c's micro-tile
-  int8_t zz[BB][BB];     // codes of this block
-};
+// descriptor: bit 63 valid | 62 far | 61 horizontal | [45,60) own | [30,45) other |
+// [15,30) last target | [0,15) first target
+__device__ inline unsigned long long pack_task(bool far, int dir, int own, int other, int t0,
+                                               int t1) {
+  return (1ull << 63) | ((unsigned long long)far << 62) | ((unsigned long long)dir << 61) |
+         ((unsigned long long)own << 45) | ((unsigned long long)other << 30) |
+         ((unsigned long long)t1 << 15) | (unsigned long long)t0;
+}
 
-// Orders the LDS accesses of one wave: the LDS unit executes a wave's operations in
-// issue order, so it is enough that the compiler keeps program order here (no wait
-// on outstanding global loads is wanted).
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+__device__ inline int ld_dev(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline bool aborted(const int* ctl) { return ld_dev(ctl + kAbort) != 0; }
+__device__ inline void abort_sweep(int* ctl, int* info) {
+  if (atomicCAS(ctl + kAbort, 0, 1) == 0) record_info(info, 4, 0);
+}
+
+// Whole-wave wait until *p >= v.  False if the sweep is aborted (or this wait times
+// out, which aborts it).
+__device__ inline bool wait_ge(const int* p, int v, int* ctl, int* info) {
+  for (int it = 0;; ++it) {
+    const int x = __builtin_amdgcn_readfirstlane(ld_dev(p));
+    if (x >= v) return true;
+    if ((it & 15) == 15) {
+      if (aborted(ctl)) return false;
+      if (it > kSpinLimit) {
+        if ((threadIdx.x & 63) == 0) abort_sweep(ctl, info);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Orders this wave's memory operations for the compiler (the hardware keeps a wave's
+// LDS operations in issue order).
 __device__ inline void lds_wave_sync() { __asm__ volatile("" ::: "memory"); }
+// Waits until every memory operation this wave issued has completed.
+__device__ inline void drain() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+template <typename T>
+__device__ inline T buf_load_dev(rsrc_t r, uint32_t elem);
+template <>
+__device__ inline float buf_load_dev<float>(rsrc_t r, uint32_t elem) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, elem * 4u, 0, kDev));
+}
+template <>
+__device__ inline double buf_load_dev<double>(rsrc_t r, uint32_t elem) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, 0, kDev);
+  return __hiloint2double((int)v[1], (int)v[0]);
+}
+template <typename T>
+__device__ inline void buf_store_dev(T v, rsrc_t r, uint32_t elem);
+template <>
+__device__ inline void buf_store_dev<float>(float v, rsrc_t r, uint32_t elem) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, elem * 4u, 0, kDev);
+}
+template <>
+__device__ inline void buf_store_dev<double>(double v, rsrc_t r, uint32_t elem) {
+  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+  const u2 x = {(unsigned)__double2loint(v), (unsigned)__double2hiint(v)};
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, elem * 8u, 0, kDev);
+}
+template <typename T>
+__device__ inline T buf_load_s_dev(rsrc_t r, uint32_t elem, uint32_t uelem);
+template <>
+__device__ inline float buf_load_s_dev<float>(rsrc_t r, uint32_t elem, uint32_t uelem) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, elem * 4u, uelem * 4u, kDev));
+}
+template <>
+__device__ inline double buf_load_s_dev<double>(rsrc_t r, uint32_t elem, uint32_t uelem) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, uelem * 8u, kDev);
+  return __hiloint2double((int)v[1], (int)v[0]);
+}
 
 __device__ inline float rint_t(float x) { return rintf(x); }
 __device__ inline double rint_t(double x) { return rint(x); }
 __device__ inline float abs_t(float x) { return fabsf(x); }
 __device__ inline double abs_t(double x) { return fabs(x); }
+__device__ inline float min_t(float a, float b) { return fminf(a, b); }
+__device__ inline double min_t(double a, double b) { return fmin(a, b); }
+__device__ inline float max_t(float a, float b) { return fmaxf(a, b); }
+__device__ inline double max_t(double a, double b) { return fmax(a, b); }
 
 template <typename T>
 struct Eps;
@@ -147,11 +280,6 @@ __device__ inline double quad_sum(double v) {
   return v + w;
 }
 
-__device__ inline float min_t(float a, float b) { return fminf(a, b); }
-__device__ inline double min_t(double a, double b) { return fmin(a, b); }
-__device__ inline float max_t(float a, float b) { return fmaxf(a, b); }
-__device__ inline double max_t(double a, double b) { return fmax(a, b); }
-
 // Four consecutive elements from LDS (16-byte aligned), as one or two vector reads.
 template <typename T>
 struct Vec4 {
@@ -168,7 +296,6 @@ __device__ inline Vec4<double> lds_read4(const double* p) {
   const d2 y = *(const d2*)(p + 2);
   return Vec4<double>{{x[0], x[1], y[0], y[1]}};
 }
-// Two consecutive elements (aligned to their pair size).
 template <typename T>
 struct Vec2 {
   T v[2];
@@ -193,383 +320,460 @@ struct StepOps {
   Vec2<T> sp;
 };
 
-// Rounds all blocks of block anti-diagonal D.  Wave w owns micro-row w (16 rows) and at
-// micro anti-diagonal d handles micro-tile (w, d - w).  In the micro sweep, lane
-// (r, q) = (lane / 4, lane % 4) works on row r; at step st the active lanes hold the
-// micro anti-diagonal r + l = st.  The target of (r, l) is
-//     t = g0[r][l] - h0[r][l] - (vertical + horizontal feedback inside the micro-tile)
-// where the two nearest terms (row r-1 at the previous step, reached by a DPP row
-// shift, and the lane's own previous Delta) are added on the critical path and the
-// older ones (rows <= r-2, columns <= l-2) are summed one step ahead from LDS, each
-// quarter q taking four of them, then reduced across the quad.
+// ---------------------------------------------------------------------------
+// band worker
+// ---------------------------------------------------------------------------
+// Row pitches keep 4-element groups 16-byte aligned for vector LDS reads.
 template <typename T>
-__global__ __launch_bounds__(256) void k_round(SweepArgs<T> a, int D) {
-  typedef typename Mfma<T>::acc_t acc_t;
-  constexpr int P = Pad<T>::v;
-  __shared__ RoundSmem<T> sm;
-  const int kmin = D - (a.Nb - 1) > 0 ? D - (a.Nb - 1) : 0;
-  const int K = kmin + blockIdx.x;
-  const int L = D - K;
-  const int64_t m = a.m, n = a.n;
-  const int64_t r0 = (int64_t)K * BB, c0 = (int64_t)L * BB;
-  const int mr = (m - r0) < BB ? (int)(m - r0) : BB;
-  const int nc = (n - c0) < BB ? (int)(n - c0) : BB;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+struct Pad;
+template <>
+struct Pad<float> {
+  static constexpr int v = 4;
+};
+template <>
+struct Pad<double> {
+  static constexpr int v = 2;
+};
 
-  // Global loads first, all in flight together: the wave's four micro-tiles of
-  // W - G and H pushed from outside (MFMA accumulator layout), the diagonal factor
-  // blocks and the scales.
-  // Reads past the block's last row come back as zero; columns past the edge read
-  // neighbouring (finite) data that only ever feeds padded entries.
+template <typename T>
+struct BandSmem {
+  static constexpr int PR = BB + Pad<T>::v;  // pitch of a transposed R column
+  static constexpr int PD = MU + Pad<T>::v;  // pitch of a Delta / U'b micro row
+  T rT[4][MU][PR];         // R ring by micro-column j % 4, transposed: rT[.][c][band row]
+  T dh[4][8][MU][PD];      // per wave, Delta ring by micro-column j % 8: dh[w][.][r][c]
+  T ubT[4][MU][PD];        // per wave: diagonal micro-block of U'b, ubT[c][k] = U'b[k][c]
+  T sup[4][MU][2];         // per wave: (U'b[c-2][c], U'b[c-1][c]) inside the micro-block
+  T g0s[4][MU][MU];        // per wave, skewed: g0s[r][sl] = (W - G outside)[r][(sl - r) % 16]
+  T h0s[4][MU][MU];        // per wave, skewed: H from outside; scratch during a sweep
+  int8_t zz[4][MU][MU];    // per wave: codes of the micro-tile
+  int bcast[4];
+};
+
+// Rounds micro-tile (w, j) of band K and stores its R, Delta, codes and Q.
+template <typename T>
+__device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, int K, int w,
+                                        int j, int ev, const T (&aVn)[BB / 4],
+                                        const T (&aVi)[3 * MU / 4], const T (&cu)[4], T cup,
+                                        T cup2, T s_r, T rs_r) {
+  typedef typename Mfma<T>::acc_t acc_t;
+  constexpr int PR = BandSmem<T>::PR, PD = BandSmem<T>::PD;
+  const int64_t m = a.m, n = a.n;
+  const int lane = threadIdx.x & 63;
+  const int kq = lane >> 4, cl = lane & 15;
+  const int64_t r0 = (int64_t)K * BB;
+  const int mr = (m - r0) < BB ? (int)(m - r0) : BB;
+  const int64_t c0 = (int64_t)j * MU;
+  const int nc = (n - c0) < MU ? (int)(n - c0) : MU;
+  const int L = j / GOUT;  // 64-wide column block
+  const int eh = expected_pushes(L);
+  const int clo = GOUT * (L > 0 ? L - 1 : 0);  // first micro-column of the local window
+  const int nwin = j - clo;                     // window micro-columns, 0..7
+  const int s4 = j & 3, s8 = j & 7;
   const int64_t es = sizeof(T);
-  const int64_t blk_bytes = ((int64_t)(mr - 1) * n + nc) * es;
-  const int64_t o0 = r0 * n + c0;
-  const rsrc_t rw = make_rsrc(a.W + o0, blk_bytes), rvf = make_rsrc(a.Vf + o0, blk_bytes);
-  const rsrc_t rhf = make_rsrc(a.Hf + o0, blk_bytes);
-  const rsrc_t rua = make_rsrc(a.Ua + r0 * m + r0, ((int64_t)(mr - 1) * m + mr) * es);
-  const rsrc_t rub = make_rsrc(a.Ub + c0 * n + c0, ((int64_t)(nc - 1) * n + nc) * es);
-  T gin[BB / MU][4], hin[BB / MU][4];
+
+  // dependencies: R of the band above for this micro-column; the pushed feedback of
+  // this 64-wide block
+  if (K > 0 && !wait_ge(a.rdone + K - 1, j + 1, a.ctl, a.info)) return;
+  if (ev > 0 && !wait_ge(a.vcnt + (int64_t)K * a.Nb + L, ev, a.ctl, a.info)) return;
+  if (eh > 0 && !wait_ge(a.hcnt + (int64_t)K * a.Nb + L, eh, a.ctl, a.info)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+  // global loads (all in flight together)
+  const int64_t row0 = r0 + MU * w;  // first row of this micro-tile
+  const int rows = mr - MU * w;      // valid rows (1..16)
+  const int64_t tile_bytes = ((int64_t)(rows - 1) * n + nc) * es;
+  const int64_t o0 = row0 * n + c0;
+  const rsrc_t rw = make_rsrc(a.W + o0, tile_bytes);
+  const rsrc_t rvf = make_rsrc(a.Vf + o0, ev > 0 ? tile_bytes : 0);
+  const rsrc_t rhf = make_rsrc(a.Hf + o0, eh > 0 ? tile_bytes : 0);
+  T gin[4], hin[4];
 #pragma unroll
-  for (int jm = 0; jm < BB / MU; ++jm)
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t o = (uint32_t)(Mfma<T>::row(lane, e) * n + cl);
+    gin[e] = buf_load<T>(rw, o) - buf_load_dev<T>(rvf, o);
+    hin[e] = buf_load_dev<T>(rhf, o);
+  }
+  // R of the band above, column block of this micro-column (k-major B operand)
+  T bnb[BB / 4];
+  {
+    const rsrc_t rr = make_rsrc(K > 0 ? a.R + (r0 - BB) * n + c0 : a.R,
+                                K > 0 ? ((int64_t)(BB - 1) * n + nc) * es : 0);
+#pragma unroll
+    for (int s = 0; s < BB / 4; ++s) bnb[s] = buf_load_dev<T>(rr, (uint32_t)((4 * s + kq) * n + cl));
+  }
+  // U'b rows of the local window, this micro-column's columns (k-major B operand)
+  T bwin[7 * MU / 4];
+  {
+    const rsrc_t rb = make_rsrc(a.Ub + (int64_t)clo * MU * n + c0,
+                                nwin > 0 ? ((int64_t)(nwin * MU - 1) * n + nc) * es : 0);
+#pragma unroll
+    for (int s = 0; s < 7 * MU / 4; ++s)
+      bwin[s] = buf_load<T>(rb, (uint32_t)((4 * s + kq) * n + cl));
+  }
+  // diagonal micro-block of U'b (strictly upper part used)
+  T ubd[MU * MU / 64];
+  {
+    const rsrc_t rb = make_rsrc(a.Ub + c0 * n + c0, ((int64_t)(nc - 1) * n + nc) * es);
+#pragma unroll
+    for (int u = 0; u < MU * MU / 64; ++u) {
+      const int idx = lane + 64 * u, k = idx >> 4, c = idx & 15;
+      ubd[u] = buf_load<T>(rb, (uint32_t)(k * n + c));
+    }
+  }
+
+  // this micro-tile's LDS: R ring rows and Delta slot start at zero; U'b diagonal block
+#pragma unroll
+  for (int u = 0; u < MU * MU / 64; ++u) {
+    const int idx = lane + 64 * u, r = idx & 15, c = idx >> 4;
+    sm.rT[s4][c][MU * w + r] = T(0);
+    sm.dh[w][s8][c][r] = T(0);
+    const int k = idx >> 4, cc = idx & 15;  // ubd[u] holds U'b[c0 + k][c0 + cc]
+    sm.ubT[w][cc][k] = (k < cc && cc < nc) ? ubd[u] : T(0);
+  }
+  lds_wave_sync();
+  if (lane < MU) {
+    sm.sup[w][lane][0] = lane >= 2 ? sm.ubT[w][lane][lane - 2] : T(0);
+    sm.sup[w][lane][1] = lane >= 1 ? sm.ubT[w][lane][lane - 1] : T(0);
+  }
+
+  // feedback from outside the micro-tile (MFMA), two chains per product
+  {
+    acc_t v0 = acc_t{0, 0, 0, 0}, v1 = acc_t{0, 0, 0, 0};
+    if (K > 0) {
+#pragma unroll
+      for (int s = 0; s < BB / 4; s += 2) {
+        v0 = Mfma<T>::run(aVn[s], bnb[s], v0);
+        v1 = Mfma<T>::run(aVn[s + 1], bnb[s + 1], v1);
+      }
+    }
+    // earlier micro-rows of this band, same micro-column (written in earlier phases)
+#pragma unroll
+    for (int s = 0; s < 3 * MU / 4; s += 2) {
+      if (s < 4 * w) {
+        v0 = Mfma<T>::run(aVi[s], sm.rT[s4][cl][4 * s + kq], v0);
+        v1 = Mfma<T>::run(aVi[s + 1], sm.rT[s4][cl][4 * s + 4 + kq], v1);
+      }
+    }
+    acc_t h0 = acc_t{0, 0, 0, 0}, h1 = acc_t{0, 0, 0, 0};
+    // the band's Delta over the window columns (this wave's rows) times U'b
+#pragma unroll
+    for (int s = 0; s < 7 * MU / 4; s += 2) {
+      if (s < 4 * nwin) {
+        const int k0 = 4 * s + kq, k1 = 4 * s + 4 + kq;
+        h0 = Mfma<T>::run(sm.dh[w][(clo + (k0 >> 4)) & 7][cl][k0 & 15], bwin[s], h0);
+        h1 = Mfma<T>::run(sm.dh[w][(clo + (k1 >> 4)) & 7][cl][k1 & 15], bwin[s + 1], h1);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = MU * w + Mfma<T>::row(lane, e), c = MU * jm + (lane & 15);
-      const uint32_t o = (uint32_t)(i * n + c);
-      gin[jm][e] = buf_load<T>(rw, o) - buf_load<T>(rvf, o);
-      hin[jm][e] = buf_load<T>(rhf, o);
-    }
-  T fua[BB * BB / 256], fub[BB * BB / 256];
-#pragma unroll
-  for (int it = 0; it < BB * BB / 256; ++it) {
-    const int idx = tid + 256 * it, i = idx >> 6, j = idx & 63;
-    fua[it] = buf_load<T>(rua, (uint32_t)(i * m + j));
-    fub[it] = buf_load<T>(rub, (uint32_t)(i * n + j));
-  }
-  // Operands of the two 64-deep neighbour pulls (block above: U'a^T R; block to the
-  // left: Delta U'b), all k-major.  The shared B panels (R and U'b rows of the
-  // previous blocks) are staged through LDS; each wave keeps its own A fragments
-  // (16 k-steps) in registers.  Buffer ranges end at the last valid element.
-  const int kq = lane >> 4, cl = lane & 15;
-  const int rows_w = mr - MU * w;
-  const int rv_w = rows_w < 0 ? 0 : (rows_w > MU ? MU : rows_w);
-  const bool up = K > 0, left = L > 0;
-  T bv_st[BB * BB / 256], bh_st[BB * BB / 256];
-  T av_fr[BB / 4], ah_fr[BB / 4];
-  {
-    const rsrc_t rbv = make_rsrc(up ? a.R + (r0 - BB) * n + c0 : a.R, up ? ((int64_t)(BB - 1) * n + nc) * es : 0);
-    const rsrc_t rbh = make_rsrc(left ? a.Ub + (c0 - BB) * n + c0 : a.Ub, left ? ((int64_t)(BB - 1) * n + nc) * es : 0);
-    const rsrc_t rav = make_rsrc(up ? a.Ua + (r0 - BB) * m + r0 + MU * w : a.Ua,
-                                 up ? ((int64_t)(BB - 1) * m + rv_w) * es : 0);
-    const rsrc_t rah = make_rsrc(left ? a.DT + (c0 - BB) * m + r0 + MU * w : a.DT,
-                                 left ? ((int64_t)(BB - 1) * m + rv_w) * es : 0);
-#pragma unroll
-    for (int it = 0; it < BB * BB / 256; ++it) {
-      const int idx = tid + 256 * it, k = idx >> 6, c = idx & 63;
-      bv_st[it] = buf_load<T>(rbv, (uint32_t)(k * n + c));
-      bh_st[it] = buf_load<T>(rbh, (uint32_t)(k * n + c));
-    }
-#pragma unroll
-    for (int sk = 0; sk < BB / 4; ++sk) {
-      av_fr[sk] = buf_load<T>(rav, (uint32_t)((4 * sk + kq) * m + cl));
-      ah_fr[sk] = buf_load<T>(rah, (uint32_t)((4 * sk + kq) * m + cl));
+      gin[e] -= v0[e] + v1[e];
+      hin[e] += h0[e] + h1[e];
     }
   }
-  const T sv0 = buf_load<T>(make_rsrc(a.s + r0, (int64_t)mr * es), (uint32_t)(tid & 63));
-  const T sv = tid < mr ? sv0 : T(1);
+  // skewed staging: slot sl of row r holds column (sl - r) mod 16
 #pragma unroll
-  for (int it = 0; it < BB * BB / 256; ++it) {
-    const int idx = tid + 256 * it, i = idx >> 6, j = idx & 63;
-    fua[it] = (i < mr && j < mr && i < j) ? fua[it] : T(0);
-    fub[it] = (i < nc && j < nc && i < j) ? fub[it] : T(0);
+  for (int e = 0; e < 4; ++e) {
+    const int row = Mfma<T>::row(lane, e), col = cl;
+    sm.g0s[w][row][(col + row) & (MU - 1)] = gin[e];
+    sm.h0s[w][row][(col + row) & (MU - 1)] = hin[e];
   }
-#pragma unroll
-  for (int it = 0; it < BB * BB / 256; ++it) {
-    const int idx = tid + 256 * it, i = idx >> 6, j = idx & 63;
-    sm.ua[i][j] = fua[it];
-    sm.ubT[j][i] = fub[it];
-    sm.rT[i][j] = bv_st[it];  // staging: R panel of the block above, rT[k][c]
-    sm.dd[i][j] = bh_st[it];  // staging: U'b panel of the block to the left, dd[k][c]
-  }
-  if (tid < BB) {
-    sm.sc[tid] = sv;
-    sm.rs[tid] = T(1) / sv;
-  }
-  __syncthreads();
-  // neighbour pulls into this wave's inputs (MFMA accumulator layout = gin/hin layout)
-  if (up) {
-    acc_t acc[BB / MU];
-#pragma unroll
-    for (int jm = 0; jm < BB / MU; ++jm) acc[jm] = acc_t{0, 0, 0, 0};
-#pragma unroll
-    for (int sk = 0; sk < BB / 4; ++sk)
-#pragma unroll
-      for (int jm = 0; jm < BB / MU; ++jm)
-        acc[jm] = Mfma<T>::run(av_fr[sk], sm.rT[4 * sk + kq][MU * jm + cl], acc[jm]);
-#pragma unroll
-    for (int jm = 0; jm < BB / MU; ++jm)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gin[jm][e] -= acc[jm][e];
-  }
-  if (left) {
-    acc_t acc[BB / MU];
-#pragma unroll
-    for (int jm = 0; jm < BB / MU; ++jm) acc[jm] = acc_t{0, 0, 0, 0};
-#pragma unroll
-    for (int sk = 0; sk < BB / 4; ++sk)
-#pragma unroll
-      for (int jm = 0; jm < BB / MU; ++jm)
-        acc[jm] = Mfma<T>::run(ah_fr[sk], sm.dd[4 * sk + kq][MU * jm + cl], acc[jm]);
-#pragma unroll
-    for (int jm = 0; jm < BB / MU; ++jm)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hin[jm][e] += acc[jm][e];
-  }
-  // coupling to columns of an earlier micro-tile is applied by the MFMA pulls, so the
-  // table is zero where l-1 or l-2 falls outside l's micro-tile
-  if (tid < BB) {
-    const int lm = tid & (MU - 1);
-    sm.sup[tid][0] = lm >= 2 ? sm.ubT[tid][tid - 2] : T(0);
-    sm.sup[tid][1] = lm >= 1 ? sm.ubT[tid][tid - 1] : T(0);
-  }
-  __syncthreads();
-  // the staging areas become this block's R and Delta, which start at zero
-#pragma unroll
-  for (int it = 0; it < BB * BB / 256; ++it) {
-    const int idx = tid + 256 * it, i = idx >> 6, j = idx & 63;
-    sm.rT[i][j] = T(0);
-    sm.dd[i][j] = T(0);
-  }
-  __syncthreads();
+  lds_wave_sync();
 
   // micro sweep lane layout: lane = 4 r + q (row r of the micro-tile, quarter q)
   const int rr_ = lane >> 2, qq = lane & 3;
-  const int gr = MU * w + rr_;  // block row handled by this lane in the micro sweep
-  const T s_r = sm.sc[gr], rs_r = sm.rs[gr];
+  T g0r[MU], h0r[MU];
+#pragma unroll
+  for (int sl = 0; sl < MU; sl += 4) {
+    const Vec4<T> gv = lds_read4(&sm.g0s[w][rr_][sl]);
+    const Vec4<T> hv4 = lds_read4(&sm.h0s[w][rr_][sl]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      g0r[sl + u] = gv.v[u];
+      h0r[sl + u] = hv4.v[u];
+    }
+  }
   const T tlo = T(a.lo), thi = T(a.hi);
   const T tol = T(4) * Eps<T>::v * T(1 << (a.bits));
-  // in-micro-tile vertical coefficients: U'a[i][r] for the quarter's rows i = 4q+u
-  // (rows >= r hold zeros), and U'a[r-1][r] for the nearest row
-  T cu[4];
+  const T* rtq = &sm.rT[s4][0][MU * w + 4 * qq];  // + PR * column
+  const T* ddq = &sm.dh[w][s8][rr_][4 * qq];
+  const T* ubq = &sm.ubT[w][0][4 * qq];          // + PD * column
+  const T* spq = &sm.sup[w][0][0];                // + 2 * column
+  // Operands of step st are read during step st - 2.  At that point rows <= r - 3
+  // (columns <= l - 3) are written and the two nearer ones still read as zero, so
+  // the LDS sums hold exactly the older terms; rows r-1, r-2 and columns l-1, l-2
+  // are added from registers (DPP row shifts and the lane's own previous Deltas).
+  auto fetch = [&](int st2) {
+    const int l2 = st2 - rr_;
+    const int lc = (l2 >= 0 && l2 < MU) ? l2 : 0;
+    StepOps<T> o;
+    o.rv = lds_read4(rtq + PR * lc);
+    o.dv = lds_read4(ddq);
+    o.bv = lds_read4(ubq + PD * lc);
+    o.sp = lds_read2(spq + 2 * lc);
+    return o;
+  };
+  StepOps<T> x0 = fetch(0);
+  StepOps<T> x1 = fetch(1);
+  lds_wave_sync();
+  // inactive lanes store into this wave's staging row, which is dead until the
+  // next micro-tile
+  T* dummy = &sm.h0s[w][rr_][0];
+  T pv = T(0), ph = T(0);
+  T rprev = T(0), rup = T(0), dprev = T(0), dprev2 = T(0);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) cu[u] = sm.ua[MU * w + 4 * qq + u][gr];
-  const T cup = (rr_ > 0) ? sm.ua[gr - 1][gr] : T(0);
-  const T cup2 = (rr_ > 1) ? sm.ua[gr - 2][gr] : T(0);
-
-  for (int d = 0; d < 2 * (BB / MU) - 1; ++d) {
-    const int j = d - w;  // micro-column of this wave's micro-tile (wave-uniform)
-    if (j >= 0 && j < BB / MU) {
-      const int mc0 = MU * j;
-      // this micro-tile's inputs are at the front of the queue; rotate (static indices)
-      T wv[4], hv[4];
+  for (int st = 0; st < 2 * MU - 1; ++st) {
+    const int l = st - rr_;
+    const bool act = (l >= 0) && (l < MU);
+    // (A) operands two steps ahead
+    StepOps<T> x2;
+    if (st + 2 < 2 * MU - 1) x2 = fetch(st + 2);
+    // (B) critical chain of this step; the second-nearest terms are ready early
+    const T pv2 = pv + cup2 * up_row(rup);      // + U'a[r-2][r] R[r-2][l]
+    const T ph2 = ph + x0.sp.v[0] * dprev2;     // + Delta[r][l-2] U'b[l-2][l]
+    rup = up_row(rprev);                        // R[r-1][l]
+    const T g = g0r[st & (MU - 1)] - (pv2 + cup * rup);
+    const T hh = h0r[st & (MU - 1)] + (ph2 + x0.sp.v[1] * dprev);
+    const T t = g - hh;
+    T z = round_quot(t, s_r, rs_r, tol);
+    z = min_t(max_t(z, tlo), thi);
+    const T qv = s_r * z;
+    const T rv_new = g - qv, dv_new = t - qv;
+    const int lw = act ? l : 0;
+    T* prt = act ? &sm.rT[s4][lw][MU * w + rr_] : dummy;
+    T* pdd = act ? &sm.dh[w][s8][rr_][lw] : dummy + 1;
+    int8_t* pzz = act ? &sm.zz[w][rr_][lw] : (int8_t*)(dummy + 2);
+    *prt = rv_new;
+    *pdd = dv_new;
+    *pzz = (int8_t)(int)z;
+    rprev = rv_new;
+    dprev2 = dprev;
+    dprev = dv_new;
+    // (C) the next step's terms other than its nearest row and column
+    if (st + 1 < 2 * MU - 1) {
+      T sv = T(0), sh = T(0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wv[e] = gin[0][e];
-        hv[e] = hin[0][e];
-#pragma unroll
-        for (int jm = 0; jm + 1 < BB / MU; ++jm) {
-          gin[jm][e] = gin[jm + 1][e];
-          hin[jm][e] = hin[jm + 1][e];
-        }
+      for (int u = 0; u < 4; ++u) {
+        sv += cu[u] * x1.rv.v[u];
+        sh += x1.dv.v[u] * x1.bv.v[u];
       }
-      // feedback from outside the micro-tile but inside the block (two MFMA chains each)
-      acc_t av0 = acc_t{0, 0, 0, 0}, av1 = acc_t{0, 0, 0, 0};
-      acc_t ah0 = acc_t{0, 0, 0, 0}, ah1 = acc_t{0, 0, 0, 0};
-      for (int k0 = 0; k0 < MU * w; k0 += 8) {
-        av0 = Mfma<T>::run(sm.ua[k0 + (lane >> 4)][MU * w + (lane & 15)],
-                           sm.rT[mc0 + (lane & 15)][k0 + (lane >> 4)], av0);
-        av1 = Mfma<T>::run(sm.ua[k0 + 4 + (lane >> 4)][MU * w + (lane & 15)],
-                           sm.rT[mc0 + (lane & 15)][k0 + 4 + (lane >> 4)], av1);
-      }
-      for (int k0 = 0; k0 < mc0; k0 += 8) {
-        ah0 = Mfma<T>::run(sm.dd[MU * w + (lane & 15)][k0 + (lane >> 4)],
-                           sm.ubT[mc0 + (lane & 15)][k0 + (lane >> 4)], ah0);
-        ah1 = Mfma<T>::run(sm.dd[MU * w + (lane & 15)][k0 + 4 + (lane >> 4)],
-                           sm.ubT[mc0 + (lane & 15)][k0 + 4 + (lane >> 4)], ah1);
-      }
-      // skewed staging: slot sl of row r holds column (sl - r) mod 16
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = Mfma<T>::row(lane, e), col = lane & 15;
-        sm.g0s[w][row][(col + row) & (MU - 1)] = wv[e] - (av0[e] + av1[e]);
-        sm.h0s[w][row][(col + row) & (MU - 1)] = hv[e] + (ah0[e] + ah1[e]);
-      }
-      lds_wave_sync();
-      T g0r[MU], h0r[MU];
-#pragma unroll
-      for (int sl = 0; sl < MU; sl += 4) {
-        const Vec4<T> gv = lds_read4(&sm.g0s[w][rr_][sl]);
-        const Vec4<T> hv4 = lds_read4(&sm.h0s[w][rr_][sl]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          g0r[sl + u] = gv.v[u];
-          h0r[sl + u] = hv4.v[u];
-        }
-      }
-      const T* rtq = &sm.rT[mc0][MU * w + 4 * qq];  // + P * column
-      const T* ddq = &sm.dd[gr][mc0 + 4 * qq];
-      const T* ubq = &sm.ubT[mc0][mc0 + 4 * qq];    // + P * column
-      const T* spq = &sm.sup[mc0][0];                // + 2 * column
-      // Operands of step st are read during step st - 2.  At that point rows <= r - 3
-      // (columns <= l - 3) are written and the two nearer ones still read as zero, so
-      // the LDS sums hold exactly the older terms; rows r-1, r-2 and columns l-1, l-2
-      // are added from registers (DPP row shifts and the lane's own previous Deltas).
-      auto fetch = [&](int st2) {
-        const int l2 = st2 - rr_;
-        const int lc = (l2 >= 0 && l2 < MU) ? l2 : 0;
-        StepOps<T> o;
-        o.rv = lds_read4(rtq + P * lc);
-        o.dv = lds_read4(ddq);
-        o.bv = lds_read4(ubq + P * lc);
-        o.sp = lds_read2(spq + 2 * lc);
-        return o;
-      };
-      StepOps<T> x0 = fetch(0);
-      StepOps<T> x1 = fetch(1);
-      lds_wave_sync();
-      // inactive lanes store into this wave's staging row, which is dead until the
-      // next micro-tile
-      T* dummy = &sm.h0s[w][rr_][0];
-      T pv = T(0), ph = T(0);
-      T rprev = T(0), rup = T(0), dprev = T(0), dprev2 = T(0);
-#pragma unroll
-      for (int st = 0; st < 2 * MU - 1; ++st) {
-        const int l = st - rr_;
-        const bool act = (l >= 0) && (l < MU);
-        // (A) operands two steps ahead
-        StepOps<T> x2;
-        if (st + 2 < 2 * MU - 1) x2 = fetch(st + 2);
-        // (B) critical chain of this step; the second-nearest terms are ready early
-        const T pv2 = pv + cup2 * up_row(rup);      // + U'a[r-2][r] R[r-2][l]
-        const T ph2 = ph + x0.sp.v[0] * dprev2;     // + Delta[r][l-2] U'b[l-2][l]
-        rup = up_row(rprev);                        // R[r-1][l]
-        const T g = g0r[st & (MU - 1)] - (pv2 + cup * rup);
-        const T hh = h0r[st & (MU - 1)] + (ph2 + x0.sp.v[1] * dprev);
-        const T t = g - hh;
-        T z = round_quot(t, s_r, rs_r, tol);
-        z = min_t(max_t(z, tlo), thi);
-        const T qv = s_r * z;
-        const T rv_new = g - qv, dv_new = t - qv;
-        const int lw = act ? l : 0;
-        T* prt = act ? &sm.rT[mc0 + lw][gr] : dummy;
-        T* pdd = act ? &sm.dd[gr][mc0 + lw] : dummy + 1;
-        int8_t* pzz = act ? &sm.zz[gr][mc0 + lw] : (int8_t*)(dummy + 2);
-        *prt = rv_new;
-        *pdd = dv_new;
-        *pzz = (int8_t)(int)z;
-        rprev = rv_new;
-        dprev2 = dprev;
-        dprev = dv_new;
-        // (C) the next step's terms other than its nearest row and column
-        if (st + 1 < 2 * MU - 1) {
-          T sv = T(0), sh = T(0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            sv += cu[u] * x1.rv.v[u];
-            sh += x1.dv.v[u] * x1.bv.v[u];
-          }
-          pv = quad_sum(sv);
-          ph = quad_sum(sh);
-        }
-        x0 = x1;
-        x1 = x2;
-        lds_wave_sync();
-      }
+      pv = quad_sum(sv);
+      ph = quad_sum(sh);
     }
-    __syncthreads();
+    x0 = x1;
+    x1 = x2;
+    lds_wave_sync();
   }
-  // R row-major; Delta transposed (DT[col][row]) for the k-major band products
-  for (int idx = tid; idx < BB * BB; idx += 256) {
-    const int i = idx >> 6, j = idx & 63;
-    if (i < mr && j < nc) {
-      const int64_t o = (r0 + i) * n + c0 + j;
-      const int z = sm.zz[i][j];
-      a.R[o] = sm.rT[j][i];
+
+  // R row-major and Delta transposed (read by other workgroups), codes and Q
+  const rsrc_t rro = make_rsrc(a.R + o0, tile_bytes);
+  const rsrc_t rdt = make_rsrc(a.DT + c0 * m + row0, ((int64_t)(nc - 1) * m + rows) * es);
+  const T* sc_base = a.s + row0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = cl, r = kq + 4 * u;  // consecutive lanes along a row
+    if (r < rows && c < nc) {
+      const int64_t o = o0 + (int64_t)r * n + c;
+      buf_store_dev<T>(sm.rT[s4][c][MU * w + r], rro, (uint32_t)(r * n + c));
+      const int z = sm.zz[w][r][c];
       a.codes[o] = (int8_t)z;
-      a.Q[o] = sm.sc[i] * T(z);
+      a.Q[o] = sc_base[r] * T(z);
     }
-    const int jt = idx >> 6, it = idx & 63;
-    if (it < mr && jt < nc) a.DT[(c0 + jt) * m + r0 + it] = sm.dd[it][jt];
+    const int r2 = cl, c2 = kq + 4 * u;  // consecutive lanes along a column
+    if (r2 < rows && c2 < nc) buf_store_dev<T>(sm.dh[w][s8][r2][c2], rdt, (uint32_t)(c2 * m + r2));
   }
 }
 
-// Depth of one LDS stage of the push GEMM: 32 doubles or 64 floats per chunk of k-rows,
-// so both element types stage the same number of bytes.
+// Publishes the band-update tasks of completed block (K, L) into slots base...
+template <typename T>
+__device__ inline void publish_block(const SweepArgs<T>& a, int K, int L, int base) {
+  int slot = base;
+  int t0, t1;
+  // near pushes first (their targets are closest), then far pushes
+  for (int far = 0; far < 2; ++far)
+    for (int dir = 0; dir < 2; ++dir) {
+      const int own = dir == 0 ? K : L, other = dir == 0 ? L : K;
+      const int nt = dir == 0 ? a.Mb : a.Nb;
+      if (far) far_range(own, nt, &t0, &t1);
+      else near_range(own, nt, &t0, &t1);
+      for (int p0 = t0; p0 <= t1; p0 += kPanel) {
+        const int p1 = p0 + kPanel - 1 < t1 ? p0 + kPanel - 1 : t1;
+        __hip_atomic_store(a.qd + slot, pack_task(far != 0, dir, own, other, p0, p1),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ++slot;
+      }
+    }
+}
+
+template <typename T>
+__device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
+  const int64_t m = a.m;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = lane >> 4, cl = lane & 15;
+  const int rr_ = lane >> 2, qq = lane & 3;
+  const int64_t es = sizeof(T);
+  for (;;) {
+    __syncthreads();
+    if (tid == 0) sm.bcast[0] = aborted(a.ctl) ? a.Mb : atomicAdd(a.ctl + kBandCtr, 1);
+    __syncthreads();
+    const int K = sm.bcast[0];
+    if (K >= a.Mb) return;
+    const int64_t r0 = (int64_t)K * BB;
+    const int mr = (m - r0) < BB ? (int)(m - r0) : BB;
+    const int nw = (mr + MU - 1) / MU;  // waves with rows
+    const int ev = expected_pushes(K);
+    // band constants of this wave: U'a blocks as MFMA A fragments, in-micro-tile
+    // vertical coefficients, the row's scale
+    // U'a rows of the band above and of this band, columns of this band
+    const rsrc_t rnb = make_rsrc(K > 0 ? a.Ua + (r0 - BB) * m + r0 : a.Ua,
+                                 K > 0 ? ((int64_t)(BB - 1) * m + mr) * es : 0);
+    const rsrc_t rbd = make_rsrc(a.Ua + r0 * m + r0, ((int64_t)(mr - 1) * m + mr) * es);
+    const int colw = MU * w + cl;  // band row of this lane's MFMA output column
+    T aVn[BB / 4], aVi[3 * MU / 4];
+#pragma unroll
+    for (int s = 0; s < BB / 4; ++s) aVn[s] = buf_load<T>(rnb, (uint32_t)((4 * s + kq) * m + colw));
+#pragma unroll
+    for (int s = 0; s < 3 * MU / 4; ++s)
+      aVi[s] = s < 4 * w ? buf_load<T>(rbd, (uint32_t)((4 * s + kq) * m + colw)) : T(0);
+    const int gr = MU * w + rr_;  // band row of this lane in the micro sweep
+    const bool rowok = gr < mr;
+    T cu[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = MU * w + 4 * qq + u;
+      const T v = buf_load<T>(rbd, (uint32_t)((int64_t)i * m + gr));
+      cu[u] = (rowok && i < gr) ? v : T(0);
+    }
+    // (row -1 and -2 offsets wrap past the range and read zero)
+    const T cup0 = buf_load<T>(rbd, (uint32_t)((int64_t)(gr - 1) * m + gr));
+    const T cup20 = buf_load<T>(rbd, (uint32_t)((int64_t)(gr - 2) * m + gr));
+    const T cup = (rowok && rr_ > 0) ? cup0 : T(0);
+    const T cup2 = (rowok && rr_ > 1) ? cup20 : T(0);
+    const T sv0 = buf_load<T>(make_rsrc(a.s + r0, (int64_t)mr * es), (uint32_t)gr);
+    const T s_r = rowok ? sv0 : T(1);
+    const T rs_r = T(1) / s_r;
+
+    const int nphase = a.Nj + nw - 1;
+    for (int p = 0; p < nphase; ++p) {
+      const int cdone = p - (nw - 1);  // micro-column completed by this phase
+      const bool closes = cdone >= 0 && ((cdone & 3) == 3 || cdone == a.Nj - 1);
+      int base = 0;
+      if (tid == 0 && closes)
+        base = atomicAdd(a.ctl + kTail, block_task_count(K, cdone / GOUT, a.Mb, a.Nb));
+      const int j = p - w;
+      if (w < nw && j >= 0 && j < a.Nj && !aborted(a.ctl))
+        round_micro_tile<T>(a, sm, K, w, j, ev, aVn, aVi, cu, cup, cup2, s_r, rs_r);
+      drain();
+      __syncthreads();
+      if (tid == 0 && cdone >= 0 && !aborted(a.ctl)) {
+        if (closes) publish_block(a, K, cdone / GOUT, base);
+        st_dev(a.rdone + K, cdone + 1);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM worker
+// ---------------------------------------------------------------------------
+// Depth of one LDS stage: 64 doubles or 128 floats per chunk of k-rows (one chunk of
+// MFMA work covers the latency of the next chunk's loads).
 template <typename T>
 struct PushKc;
 template <>
 struct PushKc<float> {
-  static constexpr int v = 64;
+  static constexpr int v = 128;
 };
 template <>
 struct PushKc<double> {
-  static constexpr int v = 32;
+  static constexpr int v = 64;
 };
-// LDS row strides (elements) of the staged operands: a multiple of 16 plus 16, so the
-// four k-rows read by one MFMA operand load start 32 dwords (f64) or 16 dwords (f32)
-// apart and fall in different banks.
-constexpr int kPanel = 2;                   // target blocks per push task
-constexpr int kPadWide = kPanel * 64 + 16;  // panel-wide operand
-constexpr int kPadNarrow = 64 + 16;         // 64-wide operand
-constexpr int kPushThreads = 512;
-constexpr int kNearPanels = (3 + kPanel - 1) / kPanel;  // near targets: at most three
+constexpr int kBM = kPanel * BB;  // output rows (target side) of a task
+constexpr int kSA = kBM + 16;     // LDS pitch of the staged A chunk (k-major)
+constexpr int kSB = BB + 16;      // LDS pitch of the staged B chunk
+constexpr int kPT = kBM + 2;      // LDS pitch of the transposed epilogue
 template <typename T>
-struct PushSmem {
+struct GemmSmem {
   static constexpr int KC = PushKc<T>::v;
-  // A rows, then B rows; also the 64 x 130 transpose stage of the epilogue
-  static constexpr int kElems = KC * (kPadWide + kPadNarrow) > 64 * 130 ? KC * (kPadWide + kPadNarrow) : 64 * 130;
+  static constexpr int kStage = KC * (kSA + kSB);
+  static constexpr int kElems = kStage > BB * kPT ? kStage : BB * kPT;
   T buf[kElems];
-  int task;
+  unsigned long long desc;
+  int bcast[4];
 };
 
-// G[x][y] = sum_{k<K} A[k*lda + x] B[k*ldb + y] for x < M <= BM, y < N <= 64 (BM = 128
-// or 256), both operands k-major, added into C: C[x*ldc + y] += G[x][y], or with `trans`
-// C[y*ldc + x] += G[x][y].  One workgroup of eight waves, two per SIMD; wave w owns rows
-// x in [w BM/8, (w+1) BM/8) as (BM/128) x 4 MFMA tiles.  Operands are staged through LDS KC k-rows at a
-// time, with the next chunk's global loads in flight in registers while the current
-// chunk is multiplied.  k-rows past K read as zero (exact buffer ranges); rows or
-// columns past M, N read neighbouring finite data that only reaches outputs that are
-// never stored.  The transposed update goes through LDS so that its stores are
-// coalesced along x.
-template <typename T, int BM>
+// G[x][y] = sum_{k<K} A[k*lda + x] B[k*ldb + y] for x < M <= kBM, y < N <= 64, both
+// operands k-major; C[x*ldc + y] (or, with `trans`, C[y*ldc + x]) becomes G, or C + G.
+// Rows x of target block x / 64 take the plain store when bit x / 64 of `first` is set
+// (the target's first contribution), else read-add-write; the old C values are loaded
+// before the products start, so their latency hides behind the MFMA work.  Four waves;
+// wave w owns rows [32 w, 32 w + 32) as 2 x 4 MFMA tiles.  Operands are staged through
+// LDS KC k-rows at a time with the next chunk's loads in flight in registers.  k-rows
+// past K read as zero
+// (exact buffer ranges); rows or columns past M, N read neighbouring finite data that
+// only reaches outputs that are never stored.  B and C are produced by other workgroups
+// of the same launch, so they are accessed at device scope.
+template <typename T>
 __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t ldb, T* C,
-                                  int64_t ldc, int M, int N, int K, bool trans,
-                                  PushSmem<T>& sm) {
+                                  int64_t ldc, int M, int N, int K, bool trans, int first,
+                                  GemmSmem<T>& sm) {
   typedef typename Mfma<T>::acc_t acc_t;
-  constexpr int BN = 64;
-  static_assert(BM == 128 || BM == 256, "panel width");
   constexpr int KC = PushKc<T>::v;
-  constexpr int SA = BM + 16, SB = kPadNarrow;
-  static_assert(SA <= kPadWide, "stage layout");
-  constexpr int TH = kPushThreads;
-  constexpr int NA = KC * BM / TH, NB = KC * BN / TH;  // staged elements per thread
-  constexpr int TM = BM / 128, TN = 4;
+  constexpr int TH = kThreads;
+  constexpr int NA = KC * kBM / TH, NB = KC * BB / TH;  // staged elements per thread
+  constexpr int TM = 2, TN = 4;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wi0 = (BM / 8) * w;
+  const int wi0 = 32 * w;
   const int kq = lane >> 4, cl = lane & 15;
   const int64_t es = sizeof(T);
   const rsrc_t ra = make_rsrc(A, ((int64_t)(K - 1) * lda + M) * es);
   const rsrc_t rb = make_rsrc(B, ((int64_t)(K - 1) * ldb + N) * es);
+  const rsrc_t rc = trans ? make_rsrc(C, ((int64_t)(N - 1) * ldc + M) * es)
+                          : make_rsrc(C, ((int64_t)(M - 1) * ldc + N) * es);
+  // old C values in the layout of the epilogue that adds to them
+  T old[TM * TN * 4];
+  if (!trans) {
+#pragma unroll
+    for (int x = 0; x < TM; ++x) {
+      const bool plain = (first >> ((wi0 + 16 * x) / BB)) & 1;
+#pragma unroll
+      for (int y = 0; y < TN; ++y)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = wi0 + 16 * x + Mfma<T>::row(lane, e), j = 16 * y + cl;
+          old[(x * TN + y) * 4 + e] =
+              plain ? T(0) : buf_load_dev<T>(rc, (uint32_t)((int64_t)i * ldc + j));
+        }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < BB * kBM / TH; ++u) {
+      const int idx = tid + TH * u, yj = idx / kBM, xi = idx % kBM;
+      const bool plain = (first >> (xi / BB)) & 1;
+      old[u] = plain ? T(0) : buf_load_dev<T>(rc, (uint32_t)((int64_t)yj * ldc + xi));
+    }
+  }
   const int nch = (K + KC - 1) / KC;
-  // thread tid stages elements tid + TH u of each chunk: k-row tid / BM + u (TH / BM),
-  // column tid % BM; the per-u and per-chunk parts of the offset are wave-uniform
-  const uint32_t va = (uint32_t)((tid / BM) * lda + tid % BM);
-  const uint32_t vb = (uint32_t)((tid / BN) * ldb + tid % BN);
-  T pa[NA], pb[NB];
-  auto fetch = [&](int c) {
+  const uint32_t va = (uint32_t)((tid / kBM) * lda + tid % kBM);
+  const uint32_t vb = (uint32_t)((tid / BB) * ldb + tid % BB);
+  // two register buffers: the loads of chunk c + 2 are issued as chunk c is staged,
+  // so they have two chunks of MFMA work to arrive
+  T pa0[NA], pb0[NB], pa1[NA], pb1[NB];
+  auto fetch = [&](int c, T (&pa)[NA], T (&pb)[NB]) {
 #pragma unroll
     for (int u = 0; u < NA; ++u)
-      pa[u] = buf_load_s<T>(ra, va, (uint32_t)((c * KC + u * (TH / BM)) * lda));
+      pa[u] = buf_load_s<T>(ra, va, (uint32_t)((c * KC + u * (TH / kBM)) * lda));
 #pragma unroll
     for (int u = 0; u < NB; ++u)
-      pb[u] = buf_load_s<T>(rb, vb, (uint32_t)((c * KC + u * (TH / BN)) * ldb));
+      pb[u] = buf_load_s_dev<T>(rb, vb, (uint32_t)((c * KC + u * (TH / BB)) * ldb));
   };
-  T* const as0 = sm.buf + (tid / BM) * SA + tid % BM;
-  T* const bs0 = sm.buf + SA * KC + (tid / BN) * SB + tid % BN;
-  auto stage = [&]() {
+  T* const as0 = sm.buf + (tid / kBM) * kSA + tid % kBM;
+  T* const bs0 = sm.buf + kSA * KC + (tid / BB) * kSB + tid % BB;
+  auto stage = [&](const T (&pa)[NA], const T (&pb)[NB]) {
 #pragma unroll
-    for (int u = 0; u < NA; ++u) as0[u * (TH / BM) * SA] = pa[u];
+    for (int u = 0; u < NA; ++u) as0[u * (TH / kBM) * kSA] = pa[u];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) bs0[u * (TH / BN) * SB] = pb[u];
+    for (int u = 0; u < NB; ++u) bs0[u * (TH / BB) * kSB] = pb[u];
   };
   acc_t acc[TM][TN];
 #pragma unroll
@@ -578,153 +782,190 @@ __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t l
     for (int y = 0; y < TN; ++y) acc[x][y] = acc_t{0, 0, 0, 0};
   auto multiply = [&]() {
     const T* as = sm.buf;
-    const T* bs = sm.buf + SA * KC;
+    const T* bs = sm.buf + kSA * KC;
 #pragma unroll 2
     for (int ks = 0; ks < KC / 4; ++ks) {
       T fa[TM], fb[TN];
 #pragma unroll
-      for (int x = 0; x < TM; ++x) fa[x] = as[(4 * ks + kq) * SA + wi0 + 16 * x + cl];
+      for (int x = 0; x < TM; ++x) fa[x] = as[(4 * ks + kq) * kSA + wi0 + 16 * x + cl];
 #pragma unroll
-      for (int y = 0; y < TN; ++y) fb[y] = bs[(4 * ks + kq) * SB + 16 * y + cl];
+      for (int y = 0; y < TN; ++y) fb[y] = bs[(4 * ks + kq) * kSB + 16 * y + cl];
 #pragma unroll
       for (int x = 0; x < TM; ++x)
 #pragma unroll
         for (int y = 0; y < TN; ++y) acc[x][y] = Mfma<T>::run(fa[x], fb[y], acc[x][y]);
     }
   };
-  fetch(0);
-  stage();
-  __syncthreads();
-  // no branches in the loop body (keeps the accumulators in place); the fetch after the
-  // last chunk reads past K, i.e. zeros, without touching memory
-  for (int c = 0; c < nch; ++c) {
-    fetch(c + 1);
+  fetch(0, pa0, pb0);
+  fetch(1, pa1, pb1);
+  // no branches in the loop body (keeps the accumulators in place); fetches past the
+  // last chunk read past K, i.e. zeros, without touching memory
+  for (int c = 0; c < nch; c += 2) {
+    stage(pa0, pb0);
+    __syncthreads();
+    fetch(c + 2, pa0, pb0);
     multiply();
     __syncthreads();
-    stage();
-    __syncthreads();
+    if (c + 1 < nch) {
+      stage(pa1, pb1);
+      __syncthreads();
+      fetch(c + 3, pa1, pb1);
+      multiply();
+      __syncthreads();
+    }
   }
   if (!trans) {
-    const rsrc_t rc = make_rsrc(C, ((int64_t)(M - 1) * ldc + N) * es);
 #pragma unroll
-    for (int x = 0; x < TM; ++x) {
-      T old[TN][4];
+    for (int x = 0; x < TM; ++x)
 #pragma unroll
       for (int y = 0; y < TN; ++y)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = wi0 + 16 * x + Mfma<T>::row(lane, e), j = 16 * y + cl;
-          old[y][e] = buf_load<T>(rc, (uint32_t)((int64_t)i * ldc + j));
+          if (i < M && j < N)
+            buf_store_dev<T>(old[(x * TN + y) * 4 + e] + acc[x][y][e], rc,
+                             (uint32_t)((int64_t)i * ldc + j));
         }
-#pragma unroll
-      for (int y = 0; y < TN; ++y)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = wi0 + 16 * x + Mfma<T>::row(lane, e), j = 16 * y + cl;
-          if (i < M && j < N) C[(int64_t)i * ldc + j] = old[y][e] + acc[x][y][e];
-        }
-    }
     return;
   }
-  // transposed: halves of 128 x-values; the owners write G^T into LDS (pitch 130), then
-  // every thread updates whole C rows
-  constexpr int PT = 128 + 2;
-  static_assert(64 * PT <= PushSmem<T>::kElems, "transpose stage");
-  const rsrc_t rc = make_rsrc(C, ((int64_t)(N - 1) * ldc + M) * es);
+  // transposed: the owners write G^T into LDS, then every thread updates whole C rows
 #pragma unroll
-  for (int h = 0; h < BM / 128; ++h) {
-    if (wi0 / 128 == h) {
+  for (int x = 0; x < TM; ++x)
 #pragma unroll
-      for (int x = 0; x < TM; ++x)
+    for (int y = 0; y < TN; ++y)
 #pragma unroll
-        for (int y = 0; y < TN; ++y)
+      for (int e = 0; e < 4; ++e) {
+        const int xi = wi0 + 16 * x + Mfma<T>::row(lane, e), yj = 16 * y + cl;
+        sm.buf[yj * kPT + xi] = acc[x][y][e];
+      }
+  __syncthreads();
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int xi = wi0 - 128 * h + 16 * x + Mfma<T>::row(lane, e), yj = 16 * y + cl;
-            sm.buf[yj * PT + xi] = acc[x][y][e];
-          }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int u = 0; u < 64 * 128 / TH; ++u) {
-      const int idx = tid + TH * u, yj = idx >> 7, xi = idx & 127;
-      const int x = 128 * h + xi;
-      const T old = buf_load<T>(rc, (uint32_t)((int64_t)yj * ldc + x));
-      if (x < M && yj < N) C[(int64_t)yj * ldc + x] = old + sm.buf[yj * PT + xi];
-    }
-    __syncthreads();
+  for (int u = 0; u < BB * kBM / TH; ++u) {
+    const int idx = tid + TH * u, yj = idx / kBM, xi = idx % kBM;
+    if (xi < M && yj < N)
+      buf_store_dev<T>(old[u] + sm.buf[yj * kPT + xi], rc, (uint32_t)((int64_t)yj * ldc + xi));
   }
+  __syncthreads();
 }
 
-// Band pushes of the blocks on diagonal D that later diagonals do not pull themselves.
-// Vertical (into Vf) from block (K, L) to row blocks t >= K+2 of column L, horizontal
-// (into Hf) from (K, L) to column blocks t >= L+2 of row K.  Targets up to the first
-// block of the next outer block take the 64-deep panel of (K, L) ("near": at most three
-// targets); beyond that, a block that closes an outer block pushes the whole outer
-// block, 256 deep.  Tasks cover kPanel target blocks each.  Workgroups take tasks
-// (panel, direction, source block) from a queue, far panels first; each target tile is
-// written by one task, so the order of tasks does not matter for the result.
 template <typename T>
-__global__ __launch_bounds__(kPushThreads) void k_push(SweepArgs<T> a, int D, int ntask, int P,
-                                                       int* queue) {
-  __shared__ PushSmem<T> sm;
-  const int kmin = D - (a.Nb - 1) > 0 ? D - (a.Nb - 1) : 0;
-  const int nblk2 = ntask / P;  // source blocks x 2 directions
+__device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
   const int64_t m = a.m, n = a.n;
+  const int tid = threadIdx.x;
   for (;;) {
-    __syncthreads();  // sm.task and the staging area are free
-    if (threadIdx.x == 0) sm.task = atomicAdd(queue + D, 1);
     __syncthreads();
-    const int task = sm.task;
-    if (task >= ntask) break;
-    const int panel = P - 1 - task / nblk2, rest = task % nblk2, dir = rest & 1;
-    const int K = kmin + (rest >> 1), L = D - K;
-    const int own = dir == 0 ? K : L;                // source block index along the push
-    const int nt = dir == 0 ? a.Mb : a.Nb;           // blocks along the push
-    const int first_next = GOUT * (own / GOUT + 1);  // first block of the next outer block
-    const int64_t ext = dir == 0 ? m : n;
-    int t0, t1, ks;
-    int64_t src0;
-    if (panel < kNearPanels) {
-      const int nlast = first_next < nt - 1 ? first_next : nt - 1;
-      t0 = own + 2 + kPanel * panel;
-      t1 = t0 + kPanel - 1 < nlast ? t0 + kPanel - 1 : nlast;
-      src0 = (int64_t)own * BB;
-      ks = (ext - src0) < BB ? (int)(ext - src0) : BB;
-    } else {
-      if (own % GOUT != GOUT - 1) continue;
-      t0 = first_next + 1 + kPanel * (panel - kNearPanels);
-      t1 = t0 + kPanel - 1 < nt - 1 ? t0 + kPanel - 1 : nt - 1;
-      src0 = (int64_t)(own - (GOUT - 1)) * BB;
-      ks = GOUT * BB;
+    if (tid < 64) {
+      // claim the next task and wait for its descriptor (whole first wave)
+      int slot = 0;
+      if (tid == 0) slot = aborted(a.ctl) ? a.total : atomicAdd(a.ctl + kHead, 1);
+      slot = __builtin_amdgcn_readfirstlane(slot);
+      unsigned long long d = 0;
+      if (slot < a.total) {
+        for (int it = 0;; ++it) {
+          d = __hip_atomic_load(a.qd + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          d = ((unsigned long long)__builtin_amdgcn_readfirstlane((int)(d >> 32)) << 32) |
+              (unsigned)__builtin_amdgcn_readfirstlane((int)d);
+          if (d >> 63) break;
+          if ((it & 15) == 15) {
+            if (aborted(a.ctl)) break;
+            if (it > kSpinLimit) {
+              if (tid == 0) abort_sweep(a.ctl, a.info);
+              break;
+            }
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      const bool go = (d >> 63) != 0;
+      int first = 0;
+      if (go) {
+        // wait until the earlier contributions to every target tile are applied
+        const bool far = (d >> 62) & 1;
+        const int dir = (d >> 61) & 1;
+        const int own = (d >> 45) & 0x7FFF, other = (d >> 30) & 0x7FFF;
+        const int t1 = (d >> 15) & 0x7FFF, t0 = d & 0x7FFF;
+        bool ok = true;
+        for (int t = t0; t <= t1 && ok; ++t) {
+          const int seq = push_seq(t, own, far);
+          int* cnt = dir == 0 ? a.vcnt + (int64_t)t * a.Nb + other : a.hcnt + (int64_t)other * a.Nb + t;
+          ok = wait_ge(cnt, seq, a.ctl, a.info);
+          if (seq == 0) first |= 1 << (t - t0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        if (!ok) d = 0;
+      }
+      if (tid == 0) {
+        sm.desc = go ? d : 0;
+        sm.bcast[0] = slot;
+        sm.bcast[1] = first;
+      }
     }
-    if (t0 > t1) continue;
-    const int64_t p0 = (int64_t)t0 * BB;  // first pushed row (dir 0) or column (dir 1)
+    __syncthreads();
+    const unsigned long long d = sm.desc;
+    if (sm.bcast[0] >= a.total) return;
+    if (!(d >> 63)) {
+      if (aborted(a.ctl)) return;
+      continue;
+    }
+    const bool far = (d >> 62) & 1;
+    const int dir = (d >> 61) & 1;
+    const int own = (d >> 45) & 0x7FFF, other = (d >> 30) & 0x7FFF;
+    const int t1 = (d >> 15) & 0x7FFF, t0 = d & 0x7FFF;
+    const int first = sm.bcast[1];
+    const int64_t ext = dir == 0 ? m : n;  // extent along the push
+    const int64_t src0 = far ? (int64_t)(own - (GOUT - 1)) * BB : (int64_t)own * BB;
+    const int ks = far ? GOUT * BB : ((ext - src0) < BB ? (int)(ext - src0) : BB);
+    const int64_t p0 = (int64_t)t0 * BB;
     const int64_t pend = (int64_t)(t1 + 1) * BB < ext ? (int64_t)(t1 + 1) * BB : ext;
-    const int PW = (int)(pend - p0);      // <= 64 kPanel
-    // vertical: Vf[p0 + x][c0 + y] += sum_k U'a[src0 + k][p0 + x] R[src0 + k][c0 + y];
-    // horizontal: Hf[r0 + y][p0 + x] += sum_k U'b[src0 + k][p0 + x] Delta^T[src0 + k][r0 + y]
-    const int64_t q0 = (int64_t)(dir == 0 ? L : K) * BB;  // the source block's other side
+    const int PW = (int)(pend - p0);
+    // vertical: Vf[p0 + x][q0 + y] += sum_k U'a[src0 + k][p0 + x] R[src0 + k][q0 + y];
+    // horizontal: Hf[q0 + y][p0 + x] += sum_k U'b[src0 + k][p0 + x] Delta^T[src0 + k][q0 + y]
+    const int64_t q0 = (int64_t)other * BB;
     const int64_t qext = dir == 0 ? n : m;
     const int QW = (qext - q0) < BB ? (int)(qext - q0) : BB;
     const T* pa = dir == 0 ? a.Ua : a.Ub;
     const T* pb = dir == 0 ? a.R : a.DT;
     const int64_t ldb = dir == 0 ? n : m;
     T* pc = dir == 0 ? a.Vf + p0 * n + q0 : a.Hf + q0 * n + p0;
-    panel_gemm<T, 64 * kPanel>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n, PW,
-                               QW, ks, dir != 0, sm);
+    panel_gemm<T>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n, PW, QW, ks,
+                  dir != 0, first, sm);
+    drain();
+    __syncthreads();
+    if (tid == 0) {
+      for (int t = t0; t <= t1; ++t) {
+        int* cnt = dir == 0 ? a.vcnt + (int64_t)t * a.Nb + other : a.hcnt + (int64_t)other * a.Nb + t;
+        st_dev(cnt, push_seq(t, own, far) + 1);
+      }
+    }
   }
 }
 
-// Vf = Hf = 0 and the push queues (one counter per diagonal) = 0.
 template <typename T>
-__global__ __launch_bounds__(256) void k_init(int64_t count, T* Vf, T* Hf, int nq, int* queue) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
-       i += (int64_t)gridDim.x * 256) {
-    Vf[i] = T(0);
-    Hf[i] = T(0);
-  }
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < nq; i += gridDim.x * 256) queue[i] = 0;
+struct SweepSmem {
+  static constexpr size_t kBand = sizeof(BandSmem<T>), kGemm = sizeof(GemmSmem<T>);
+  static constexpr size_t kBytes = kBand > kGemm ? kBand : kGemm;
+};
+
+// The persistent sweep: workgroups draw a ticket when they start; ticket 0 and tickets
+// beyond the band workers take band-update tasks, the others own bands (and take tasks
+// once no band is left).  Ticket 0 being a GEMM worker guarantees that tasks make
+// progress however many workgroups are resident.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_sweep(SweepArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char smem[SweepSmem<T>::kBytes];
+  __shared__ int ticket;
+  if (threadIdx.x == 0) ticket = atomicAdd(a.ctl + kTicket, 1);
+  __syncthreads();
+  const int tk = ticket;
+  if (tk >= 1 && tk <= a.nbw) band_worker<T>(a, *reinterpret_cast<BandSmem<T>*>(smem));
+  gemm_worker<T>(a, *reinterpret_cast<GemmSmem<T>*>(smem));
+}
+
+// control words, progress counters and task descriptors start at zero
+__global__ __launch_bounds__(256) void k_init_sync(int* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * 256)
+    p[i] = 0;
 }
 
 template <typename T>
@@ -736,68 +977,24 @@ __global__ __launch_bounds__(256) void k_check_scales(int64_t m, const T* __rest
   if (!(v > T(0)) || !isfinite(v)) record_info(info, 3, (int)(i + 1));
 }
 
-// Algorithmic work of one launch (only evaluated while the measurement hook is on).
-// Round: in-block feedback flops, the two 64-deep neighbour pulls (2 M N K), and the
-// HBM bytes every block must move (W, Vf, Hf, the neighbour panels, the diagonal
-// factor blocks and scales in; R, Delta, Q out, one byte per code).
-void round_work(int64_t m, int64_t n, int D, int Mb, int Nb, double es, double* flops,
-                double* bytes) {
-  *flops = *bytes = 0.0;
-  const int kmin = D - (Nb - 1) > 0 ? D - (Nb - 1) : 0;
-  const int kmax = D < Mb - 1 ? D : Mb - 1;
-  for (int K = kmin; K <= kmax; ++K) {
-    const int L = D - K;
-    const double mr = (double)((m - (int64_t)K * BB) < BB ? (m - (int64_t)K * BB) : BB);
-    const double nc = (double)((n - (int64_t)L * BB) < BB ? (n - (int64_t)L * BB) : BB);
-    *flops += mr * nc * (mr + nc - 2.0);
-    *bytes += es * (6.0 * mr * nc + mr * mr + nc * nc + mr) + mr * nc;
-    if (K > 0) {
-      *flops += 2.0 * mr * nc * BB;
-      *bytes += es * (BB * mr + BB * nc);
-    }
-    if (L > 0) {
-      *flops += 2.0 * mr * nc * BB;
-      *bytes += es * (BB * mr + BB * nc);
-    }
-  }
-}
-
-// Push: dense GEMM flops (2 M N K per tile) and operand/RMW bytes of k_push at D.
-// Returns false when no block on D has anything to push.
-bool push_work(int64_t m, int64_t n, int D, int Mb, int Nb, double es, double* flops,
-               double* bytes) {
-  *flops = *bytes = 0.0;
-  bool any = false;
-  const int kmin = D - (Nb - 1) > 0 ? D - (Nb - 1) : 0;
-  const int kmax = D < Mb - 1 ? D : Mb - 1;
-  auto ext = [](int64_t total, int64_t start) {
-    return (double)((total - start) < BB ? (total - start) : BB);
-  };
-  for (int K = kmin; K <= kmax; ++K) {
-    const int L = D - K;
-    const double nc = ext(n, (int64_t)L * BB), mr = ext(m, (int64_t)K * BB);
-    for (int t = K + 2; t < Mb; ++t) {
-      double ks;
-      if (t <= GOUT * (K / GOUT + 1)) ks = mr;
-      else if (K % GOUT == GOUT - 1) ks = GOUT * BB;
-      else continue;
-      any = true;
-      const double M = ext(m, (int64_t)t * BB);
-      *flops += 2.0 * M * nc * ks;
-      *bytes += es * (ks * M + ks * nc + 2.0 * M * nc);
-    }
-    for (int t = L + 2; t < Nb; ++t) {
-      double ks;
-      if (t <= GOUT * (L / GOUT + 1)) ks = nc;
-      else if (L % GOUT == GOUT - 1) ks = GOUT * BB;
-      else continue;
-      any = true;
-      const double N = ext(n, (int64_t)t * BB);
-      *flops += 2.0 * mr * N * ks;
-      *bytes += es * (mr * ks + ks * N + 2.0 * mr * N);
-    }
-  }
-  return any;
+struct SyncLayout {
+  int64_t ctl, rdone, vcnt, hcnt, qd, words;  // offsets in ints; qd 8-byte aligned
+  int total;
+};
+SyncLayout sync_layout(int64_t m, int64_t n) {
+  const int Mb = (int)cdiv(m, BB), Nb = (int)cdiv(n, BB);
+  int64_t total = 0;
+  for (int K = 0; K < Mb; ++K)
+    for (int L = 0; L < Nb; ++L) total += block_task_count(K, L, Mb, Nb);
+  SyncLayout s;
+  s.ctl = 0;
+  s.rdone = kCtlWords;
+  s.vcnt = s.rdone + Mb;
+  s.hcnt = s.vcnt + (int64_t)Mb * Nb;
+  s.qd = (s.hcnt + (int64_t)Mb * Nb + 1) / 2 * 2;
+  s.words = s.qd + 2 * total;
+  s.total = (int)total;
+  return s;
 }
 
 template <typename T>
@@ -815,6 +1012,7 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   a.n = n;
   a.Mb = (int)cdiv(m, BB);
   a.Nb = (int)cdiv(n, BB);
+  a.Nj = (int)cdiv(n, MU);
   a.lo = -(1 << (bits - 1));
   a.hi = (1 << (bits - 1)) - 1;
   a.bits = bits;
@@ -826,82 +1024,52 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   a.Hf = take();
   a.R = take();
   a.DT = take();
-  int* queue = (int*)c;  // [Mb + Nb - 1] push-task counters
+  const SyncLayout sl = sync_layout(m, n);
+  int* sync = (int*)c;
+  a.ctl = sync + sl.ctl;
+  a.rdone = sync + sl.rdone;
+  a.vcnt = sync + sl.vcnt;
+  a.hcnt = sync + sl.hcnt;
+  a.qd = (unsigned long long*)(sync + sl.qd);
+  a.total = sl.total;
   a.codes = codes;
   a.Q = Q;
-  const int Mb = a.Mb, Nb = a.Nb, nD = Mb + Nb - 1;
+  a.info = info;
 
-  std::lock_guard<std::recursive_mutex> lock(lib_mutex());
-  hipStream_t s1 = nullptr;
-  hipEvent_t* evs = nullptr;
-  // events 0..1 belong to the caller of this function; the sweep uses the rest
-  hipError_t e = aux_resources(2 + 2 * (size_t)nD + 1, &s1, &evs);
-  if (e != hipSuccess) return e;
-  hipEvent_t* ev_round = evs + 2;      // [nD]
-  hipEvent_t* ev_far = ev_round + nD;  // [nD]
-  hipEvent_t ev_init = ev_far[nD];
-  hipStream_t sr = s, sp = s1;
+  int dev = 0, ncu = 0, occ = 0;
+  hipError_t e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_sweep<T>, kThreads, 0)) !=
+      hipSuccess)
+    return e;
+  if (occ < 1) return hipErrorInvalidConfiguration;
+  const int grid = ncu * occ;
+  // Band workers: enough for the bands that are active at once (a band runs Nj + 3
+  // phases, the next one starts about four phases later), at most half the grid.
+  int nbw = (a.Nj + 3) / GOUT + 2;
+  if (nbw > a.Mb) nbw = a.Mb;
+  if (nbw > grid / 2) nbw = grid / 2;
+  if (nbw < 1) nbw = 1;
+  a.nbw = nbw;
+
   const bool pr = prof_on();
   const double es = (double)sizeof(T);
   prof_begin(KC_OTHER, s);
   k_check_scales<T><<<(unsigned)cdiv(m, 256), 256, 0, s>>>(m, scales, info);
-  const int64_t ig = cdiv((int64_t)mn, 256) < 8192 ? cdiv((int64_t)mn, 256) : 8192;
-  k_init<T><<<(unsigned)ig, 256, 0, s>>>((int64_t)mn, a.Vf, a.Hf, nD, queue);
-  prof_end(KC_OTHER, s, 0.0, es * (2.0 * (double)mn + (double)m));
-  if ((e = hipEventRecord(ev_init, s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(sp, ev_init, 0)) != hipSuccess) return e;
-
-  int last_far = -1;
-  const int maxt = (Mb > Nb ? Mb : Nb);
-  // push panels per (source block, direction): near panels + far panels of kPanel blocks
-  const int P = kNearPanels + (maxt + kPanel - 1) / kPanel;
-  // The push GEMM holds more LDS than a CU can share with a rounding block, so capping
-  // its grid at (CUs - blocks of the longest diagonal) keeps CUs free for the rounding
-  // chain, whose latency-bound waves would otherwise share their SIMDs.
-  int push_grid = 0;
-  {
-    int dev = 0, ncu = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) !=
-        hipSuccess)
-      return e;
-    const int maxblk = Mb < Nb ? Mb : Nb;
-    const int keep = maxblk < ncu / 2 ? maxblk : ncu / 2;
-    push_grid = ncu - keep > 1 ? ncu - keep : 1;
-  }
-  std::vector<int> far_list;  // diagonals that issued pushes, increasing
-  size_t fp = 0;
-  int waited = -1;
-  for (int D = 0; D < nD; ++D) {
-    const int kmin = D - (Nb - 1) > 0 ? D - (Nb - 1) : 0;
-    const int kmax = D < Mb - 1 ? D : Mb - 1;
-    const int nblk = kmax - kmin + 1;
-    // pushes issued at D-2 or earlier may target blocks on D (the second stream runs
-    // them in order, so waiting for the newest such launch covers all of them)
-    while (fp < far_list.size() && far_list[fp] <= D - 2) ++fp;
-    if (fp > 0 && far_list[fp - 1] != waited) {
-      waited = far_list[fp - 1];
-      if ((e = hipStreamWaitEvent(sr, ev_far[waited], 0)) != hipSuccess) return e;
-    }
-    double fl = 0.0, by = 0.0;
-    if (pr) round_work(m, n, D, Mb, Nb, es, &fl, &by);
-    prof_begin(KC_ROUND, sr);
-    k_round<T><<<nblk, 256, 0, sr>>>(a, D);
-    prof_end(KC_ROUND, sr, fl, by);
-    if (!push_work(m, n, D, Mb, Nb, es, &fl, &by)) continue;
-    if ((e = hipEventRecord(ev_round[D], sr)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(sp, ev_round[D], 0)) != hipSuccess) return e;
-    const int ntask = nblk * 2 * P;
-    const int grid = ntask < push_grid ? ntask : push_grid;
-    prof_begin(KC_FAR, sp);
-    k_push<T><<<grid, kPushThreads, 0, sp>>>(a, D, ntask, P, queue);
-    prof_end(KC_FAR, sp, fl, by);
-    if ((e = hipEventRecord(ev_far[D], sp)) != hipSuccess) return e;
-    far_list.push_back(D);
-    last_far = D;
-  }
-  // the call completes on the caller's stream only after the push stream drains
-  if (last_far >= 0 && (e = hipStreamWaitEvent(s, ev_far[last_far], 0)) != hipSuccess) return e;
+  const int64_t ig = cdiv(sl.words, 256) < 4096 ? cdiv(sl.words, 256) : 4096;
+  k_init_sync<<<(unsigned)ig, 256, 0, s>>>(sync, sl.words);
+  prof_end(KC_OTHER, s, 0.0, 4.0 * (double)sl.words + es * (double)m);
+  // algorithmic work of the sweep: every entry takes its k vertical and l horizontal
+  // feedback terms (2 flops each); HBM bytes: W, the factors and scales in, codes and
+  // Q out, and R, Delta written once and read back by the band products
+  const double fl = pr ? (double)m * (double)n * (double)(m + n - 2) : 0.0;
+  const double by = pr ? es * (3.0 * (double)mn + (double)m * m + (double)n * n + (double)m) +
+                             (double)mn : 0.0;
+  prof_begin(KC_ROUND, s);
+  k_sweep<T><<<grid, kThreads, 0, s>>>(a);
+  prof_end(KC_ROUND, s, fl, by);
   return hipGetLastError();
 }
 
@@ -909,8 +1077,8 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
 
 size_t sweep_workspace(int64_t m, int64_t n, int dtype) {
   const size_t es = dtype == 0 ? sizeof(float) : sizeof(double);
-  const size_t nD = (size_t)(cdiv(m, BB) + cdiv(n, BB) - 1);
-  return 4 * align_up((size_t)m * n * es) + align_up(nD * sizeof(int));
+  const SyncLayout sl = sync_layout(m, n);
+  return 4 * align_up((size_t)m * n * es) + align_up((size_t)sl.words * sizeof(int));
 }
 
 hipError_t sweep_enqueue(int64_t m, int64_t n, int bits, int dtype, const void* W,
