@@ -31,9 +31,11 @@
  *     on the host before any HIP call; a positive GPTQ2D_ERR_* code when a HIP
  *     runtime call fails.  Numerical failures are reported through `info`, a
  *     DEVICE int[2] that the call first clears (may be NULL): info[0] = 1 if A is
- *     not positive definite, 2 if B is not, 3 if a scale is <= 0 or not finite;
- *     info[1] = 1-based index of the failing pivot or row.  When info[0] != 0 the
- *     outputs are undefined.
+ *     not positive definite, 2 if B is not, 3 if a scale is <= 0 or not finite,
+ *     4 if a dependency wait inside the persistent sweep kernel exceeded its bound
+ *     (the kernel then stops early instead of hanging; this only happens when the
+ *     device cannot keep the kernel's workgroups resident); info[1] = 1-based index
+ *     of the failing pivot or row.  When info[0] != 0 the outputs are undefined.
  *   - workspace: DEVICE scratch of at least the size returned by the matching
  *     *_workspace_bytes function, 256-byte aligned.  Passing NULL and 0 makes the
  *     library allocate (and free) it stream-ordered on `stream`.

@@ -676,52 +676,46 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
 // ---------------------------------------------------------------------------
 // GEMM worker
 // ---------------------------------------------------------------------------
-// Depth of one LDS stage: 64 doubles or 128 floats per chunk of k-rows (one chunk of
-// MFMA work covers the latency of the next chunk's loads).
-template <typename T>
-struct PushKc;
-template <>
-struct PushKc<float> {
-  static constexpr int v = 128;
-};
-template <>
-struct PushKc<double> {
-  static constexpr int v = 64;
-};
+// The band-update tile: C (kBM x 64) += A^T B with both operands k-major, staged through
+// LDS in chunks of kKC k-rows.  Up to three chunks of loads are kept in flight in
+// registers (12 eight-byte loads per thread per chunk, so together with the 32 old C
+// values no wave ever has more than 63 loads outstanding, the hardware counter's limit);
+// two LDS stages let the next chunk be written while the current one is multiplied.
+constexpr int kKC = 16;           // k-rows per chunk
+constexpr int kAheadMax = 3;      // chunks whose loads are in flight (long tasks)
 constexpr int kBM = kPanel * BB;  // output rows (target side) of a task
 constexpr int kSA = kBM + 16;     // LDS pitch of the staged A chunk (k-major)
 constexpr int kSB = BB + 16;      // LDS pitch of the staged B chunk
 constexpr int kPT = kBM + 2;      // LDS pitch of the transposed epilogue
+constexpr int kStageElems = kKC * (kSA + kSB);
 template <typename T>
 struct GemmSmem {
-  static constexpr int KC = PushKc<T>::v;
-  static constexpr int kStage = KC * (kSA + kSB);
-  static constexpr int kElems = kStage > BB * kPT ? kStage : BB * kPT;
+  static constexpr int kElems = 2 * kStageElems > BB * kPT ? 2 * kStageElems : BB * kPT;
   T buf[kElems];
   unsigned long long desc;
   int bcast[4];
 };
 
-// G[x][y] = sum_{k<K} A[k*lda + x] B[k*ldb + y] for x < M <= kBM, y < N <= 64, both
-// operands k-major; C[x*ldc + y] (or, with `trans`, C[y*ldc + x]) becomes G, or C + G.
+// G[x][y] = sum_{k<K} A[k*lda + x] B[k*ldb + y] for x < M <= kBM, y < N <= 64, K <= kKC NCH,
+// both operands k-major; C[x*ldc + y] (or, with `trans`, C[y*ldc + x]) becomes G, or C + G.
 // Rows x of target block x / 64 take the plain store when bit x / 64 of `first` is set
 // (the target's first contribution), else read-add-write; the old C values are loaded
-// before the products start, so their latency hides behind the MFMA work.  Four waves;
-// wave w owns rows [32 w, 32 w + 32) as 2 x 4 MFMA tiles.  Operands are staged through
-// LDS KC k-rows at a time with the next chunk's loads in flight in registers.  k-rows
-// past K read as zero
-// (exact buffer ranges); rows or columns past M, N read neighbouring finite data that
-// only reaches outputs that are never stored.  B and C are produced by other workgroups
-// of the same launch, so they are accessed at device scope.
-template <typename T>
+// while the last chunks are multiplied.  Four waves; wave w owns rows [32 w, 32 w + 32) as
+// 2 x 4 MFMA tiles.  k-rows past K read as zero (exact buffer ranges); rows or columns
+// past M, N read neighbouring finite data that only reaches outputs that are never
+// stored.  B and C are produced by other workgroups of the same launch, so they are
+// accessed at device scope.  The chunk loop is unrolled (NCH is a compile-time count), so
+// every wait for a chunk's loads is exact.
+template <typename T, int NCH>
 __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t ldb, T* C,
                                   int64_t ldc, int M, int N, int K, bool trans, int first,
                                   GemmSmem<T>& sm) {
   typedef typename Mfma<T>::acc_t acc_t;
-  constexpr int KC = PushKc<T>::v;
   constexpr int TH = kThreads;
-  constexpr int NA = KC * kBM / TH, NB = KC * BB / TH;  // staged elements per thread
+  constexpr int NA = kKC * kBM / TH, NB = kKC * BB / TH;  // staged elements per thread
   constexpr int TM = 2, TN = 4;
+  constexpr int NOLD = TM * TN * 4;
+  static_assert(NA + NB == 12 && BB * kBM / TH == NOLD, "tile shape");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi0 = 32 * w;
   const int kq = lane >> 4, cl = lane & 15;
@@ -730,61 +724,64 @@ __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t l
   const rsrc_t rb = make_rsrc(B, ((int64_t)(K - 1) * ldb + N) * es);
   const rsrc_t rc = trans ? make_rsrc(C, ((int64_t)(N - 1) * ldc + M) * es)
                           : make_rsrc(C, ((int64_t)(M - 1) * ldc + N) * es);
-  // old C values in the layout of the epilogue that adds to them
-  T old[TM * TN * 4];
-  if (!trans) {
-#pragma unroll
-    for (int x = 0; x < TM; ++x) {
-      const bool plain = (first >> ((wi0 + 16 * x) / BB)) & 1;
-#pragma unroll
-      for (int y = 0; y < TN; ++y)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = wi0 + 16 * x + Mfma<T>::row(lane, e), j = 16 * y + cl;
-          old[(x * TN + y) * 4 + e] =
-              plain ? T(0) : buf_load_dev<T>(rc, (uint32_t)((int64_t)i * ldc + j));
-        }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < BB * kBM / TH; ++u) {
-      const int idx = tid + TH * u, yj = idx / kBM, xi = idx % kBM;
-      const bool plain = (first >> (xi / BB)) & 1;
-      old[u] = plain ? T(0) : buf_load_dev<T>(rc, (uint32_t)((int64_t)yj * ldc + xi));
-    }
-  }
-  const int nch = (K + KC - 1) / KC;
   const uint32_t va = (uint32_t)((tid / kBM) * lda + tid % kBM);
   const uint32_t vb = (uint32_t)((tid / BB) * ldb + tid % BB);
-  // two register buffers: the loads of chunk c + 2 are issued as chunk c is staged,
-  // so they have two chunks of MFMA work to arrive
-  T pa0[NA], pb0[NB], pa1[NA], pb1[NB];
-  auto fetch = [&](int c, T (&pa)[NA], T (&pb)[NB]) {
+  // short tasks load the old C values first (their latency then spans the whole task)
+  // and keep two chunks in flight; long tasks keep three and load C near the end
+  constexpr int kAhead = NCH > 4 ? kAheadMax : 2;
+  constexpr int kOld = NCH > 4 ? NCH - 1 - kAhead : -1;
+  T pa[kAhead][NA], pb[kAhead][NB];
+  auto fetch = [&](int c, int r) {
 #pragma unroll
     for (int u = 0; u < NA; ++u)
-      pa[u] = buf_load_s<T>(ra, va, (uint32_t)((c * KC + u * (TH / kBM)) * lda));
+      pa[r][u] = buf_load_s<T>(ra, va, (uint32_t)((c * kKC + u * (TH / kBM)) * lda));
 #pragma unroll
     for (int u = 0; u < NB; ++u)
-      pb[u] = buf_load_s_dev<T>(rb, vb, (uint32_t)((c * KC + u * (TH / BB)) * ldb));
+      pb[r][u] = buf_load_s_dev<T>(rb, vb, (uint32_t)((c * kKC + u * (TH / BB)) * ldb));
   };
-  T* const as0 = sm.buf + (tid / kBM) * kSA + tid % kBM;
-  T* const bs0 = sm.buf + kSA * KC + (tid / BB) * kSB + tid % BB;
-  auto stage = [&](const T (&pa)[NA], const T (&pb)[NB]) {
+  auto stage = [&](int r, int st) {
+    T* as0 = sm.buf + st * kStageElems + (tid / kBM) * kSA + tid % kBM;
+    T* bs0 = sm.buf + st * kStageElems + kSA * kKC + (tid / BB) * kSB + tid % BB;
 #pragma unroll
-    for (int u = 0; u < NA; ++u) as0[u * (TH / kBM) * kSA] = pa[u];
+    for (int u = 0; u < NA; ++u) as0[u * (TH / kBM) * kSA] = pa[r][u];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) bs0[u * (TH / BB) * kSB] = pb[u];
+    for (int u = 0; u < NB; ++u) bs0[u * (TH / BB) * kSB] = pb[r][u];
+  };
+  // old C values in the layout of the epilogue that adds to them
+  T old[NOLD];
+  auto load_old = [&]() {
+    if (!trans) {
+#pragma unroll
+      for (int x = 0; x < TM; ++x) {
+        const bool plain = (first >> ((wi0 + 16 * x) / BB)) & 1;
+#pragma unroll
+        for (int y = 0; y < TN; ++y)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = wi0 + 16 * x + Mfma<T>::row(lane, e), j = 16 * y + cl;
+            old[(x * TN + y) * 4 + e] =
+                plain ? T(0) : buf_load_dev<T>(rc, (uint32_t)((int64_t)i * ldc + j));
+          }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NOLD; ++u) {
+        const int idx = tid + TH * u, yj = idx / kBM, xi = idx % kBM;
+        const bool plain = (first >> (xi / BB)) & 1;
+        old[u] = plain ? T(0) : buf_load_dev<T>(rc, (uint32_t)((int64_t)yj * ldc + xi));
+      }
+    }
   };
   acc_t acc[TM][TN];
 #pragma unroll
   for (int x = 0; x < TM; ++x)
 #pragma unroll
     for (int y = 0; y < TN; ++y) acc[x][y] = acc_t{0, 0, 0, 0};
-  auto multiply = [&]() {
-    const T* as = sm.buf;
-    const T* bs = sm.buf + kSA * KC;
-#pragma unroll 2
-    for (int ks = 0; ks < KC / 4; ++ks) {
+  auto multiply = [&](int st) {
+    const T* as = sm.buf + st * kStageElems;
+    const T* bs = as + kSA * kKC;
+#pragma unroll
+    for (int ks = 0; ks < kKC / 4; ++ks) {
       T fa[TM], fb[TN];
 #pragma unroll
       for (int x = 0; x < TM; ++x) fa[x] = as[(4 * ks + kq) * kSA + wi0 + 16 * x + cl];
@@ -796,23 +793,21 @@ __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t l
         for (int y = 0; y < TN; ++y) acc[x][y] = Mfma<T>::run(fa[x], fb[y], acc[x][y]);
     }
   };
-  fetch(0, pa0, pb0);
-  fetch(1, pa1, pb1);
-  // no branches in the loop body (keeps the accumulators in place); fetches past the
-  // last chunk read past K, i.e. zeros, without touching memory
-  for (int c = 0; c < nch; c += 2) {
-    stage(pa0, pb0);
-    __syncthreads();
-    fetch(c + 2, pa0, pb0);
-    multiply();
-    __syncthreads();
-    if (c + 1 < nch) {
-      stage(pa1, pb1);
-      __syncthreads();
-      fetch(c + 3, pa1, pb1);
-      multiply();
-      __syncthreads();
+  if (kOld < 0) load_old();
+#pragma unroll
+  for (int c = 0; c < kAhead && c < NCH; ++c) fetch(c, c);
+  stage(0, 0);
+  if (kAhead < NCH) fetch(kAhead, 0);
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c + 1 < NCH) {
+      stage((c + 1) % kAhead, (c + 1) & 1);
+      if (c + 1 + kAhead < NCH) fetch(c + 1 + kAhead, (c + 1) % kAhead);
     }
+    if (c == kOld) load_old();
+    multiply(c & 1);
+    __syncthreads();
   }
   if (!trans) {
 #pragma unroll
@@ -840,7 +835,7 @@ __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t l
       }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < BB * kBM / TH; ++u) {
+  for (int u = 0; u < NOLD; ++u) {
     const int idx = tid + TH * u, yj = idx / kBM, xi = idx % kBM;
     if (xi < M && yj < N)
       buf_store_dev<T>(old[u] + sm.buf[yj * kPT + xi], rc, (uint32_t)((int64_t)yj * ldc + xi));
@@ -927,8 +922,12 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
     const T* pb = dir == 0 ? a.R : a.DT;
     const int64_t ldb = dir == 0 ? n : m;
     T* pc = dir == 0 ? a.Vf + p0 * n + q0 : a.Hf + q0 * n + p0;
-    panel_gemm<T>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n, PW, QW, ks,
-                  dir != 0, first, sm);
+    if (far)
+      panel_gemm<T, GOUT * BB / kKC>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n,
+                                     PW, QW, ks, dir != 0, first, sm);
+    else
+      panel_gemm<T, BB / kKC>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n, PW,
+                              QW, ks, dir != 0, first, sm);
     drain();
     __syncthreads();
     if (tid == 0) {
