@@ -3,8 +3,9 @@
 One step = the whole hot path on inputs already resident in HBM: factor A, factor B,
 anti-diagonal sweep (gptq2d_quantize).  Prints one JSON line with
   value = quantized weight entries / second (m*n / seconds per layer),
-  roofline = the dominant kernel class against its MI355X peak (per-launch durations
-             from HIP events recorded on the launch stream by the library's hook),
+  roofline = the dominant kernel (the persistent sweep) against its MI355X peak: the
+             recurrence's flops m n (m + n - 2) over the launch duration from HIP events
+             recorded on the launch stream by the library's hook,
   cpu_baseline = the CPU oracle on a bounded sample of the same layer.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3]
 """
@@ -37,10 +38,10 @@ def source_digest():
 
 
 def stored_traffic(workload, dtype):
-    """HBM bytes per launch of the rounding kernel from the committed counter summary
+    """HBM bytes per launch of the sweep kernel from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy kernel), or None when the summary
     is missing or was taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"pmc_round_{workload.lower()}_{dtype}.md")
+    path = os.path.join(ROOT, "profiles", f"pmc_sweep_{workload.lower()}_{dtype}.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -190,21 +191,30 @@ def main():
         }
     log("[bench] per-kernel: " + json.dumps(kernels))
     gemm_peak = PEAK["fp32_tflops"] if args.dtype == "f32" else PEAK["fp64_tflops"]
-    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    timed = [k for k in kernels if k != "band_gemm"]
+    dominant = max(timed, key=lambda k: kernels[k]["ms_per_step"])
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
 
     def roof(name):
         k = kernels[name]
-        if name in ("near", "far"):
+        if name == "sweep":
+            # the whole sweep kernel: algorithmic flops of the recurrence per launch over
+            # the launch's event-timed duration, against the MFMA peak of its dtype
             return {"kernel": name, "bound": "mfma", "achieved": k["tflops"], "peak": gemm_peak,
-                    "unit": "TFLOP/s", "frac": k["tflops"] / gemm_peak, "traffic": None}
-        if name in ("trailing", "trtri", "panel", "potrf", "chol"):
-            return {"kernel": name, "bound": "mfma", "achieved": k["tflops"],
-                    "peak": PEAK["fp64_tflops"], "unit": "TFLOP/s",
-                    "frac": k["tflops"] / PEAK["fp64_tflops"], "traffic": None}
-        traffic = stored_traffic(wl.name, args.dtype) if name == "round" else None
-        return {"kernel": name, "bound": "hbm", "achieved": k["gbs"], "peak": PEAK["hbm_gbs"],
-                "unit": "GB/s", "frac": k["gbs"] / PEAK["hbm_gbs"], "traffic": traffic,
-                "algorithmic_bytes_per_launch": k["bytes_per_launch"]}
+                    "unit": "TFLOP/s", "frac": k["tflops"] / gemm_peak,
+                    "traffic": stored_traffic(wl.name, args.dtype),
+                    "algorithmic_flops_per_launch": k["flops_per_launch"],
+                    "algorithmic_bytes_per_launch": k["bytes_per_launch"]}
+        if name == "band_gemm":
+            # band-update GEMM tasks inside the sweep: dense flops over the busy time of
+            # the workgroups running them (CU-seconds), scaled to all CUs of the device
+            rate = k["flops_per_launch"] * k["launches_per_step"] / (k["ms_per_step"] / 1e3) / 1e12
+            return {"kernel": name, "bound": "mfma", "achieved": rate * ncu, "peak": gemm_peak,
+                    "unit": "TFLOP/s (per busy CU x CUs)", "frac": rate * ncu / gemm_peak,
+                    "traffic": None, "tasks_per_step": k["launches_per_step"]}
+        return {"kernel": name, "bound": "mfma", "achieved": k["tflops"],
+                "peak": PEAK["fp64_tflops"], "unit": "TFLOP/s",
+                "frac": k["tflops"] / PEAK["fp64_tflops"], "traffic": None}
 
     z_gpu = codes.cpu().numpy().astype(np.int32)
     alt = None
@@ -242,7 +252,8 @@ def main():
                                f"{args.dtype} sweep, fp64 factor", "m": m, "n": n,
                    "bits": wl.bits, "recipe": wl.recipe},
         "roofline": roof(dominant),
-        "rooflines": [roof(k) for k in sorted(kernels, key=lambda k: -kernels[k]["ms_per_step"])],
+        "rooflines": [roof(k) for k in sorted(kernels, key=lambda k: -kernels[k]["ms_per_step"])
+                      if k != "other"],
         "kernels": kernels,
         "cpu_baseline": cpu,
         "other_dtype": alt,

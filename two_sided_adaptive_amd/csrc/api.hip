@@ -296,6 +296,14 @@ int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* fl
     p.pool.push_back(e.b);
   }
   p.pending.clear();
+  {
+    double cu_ms = 0.0, fl = 0.0;
+    int64_t tasks = 0;
+    if (g2d::band_stats_collect(&cu_ms, &fl, &tasks) != hipSuccess) rc = GPTQ2D_ERR_HIP;
+    p.ms[g2d::KC_BAND_GEMM] += cu_ms;
+    p.flops[g2d::KC_BAND_GEMM] += fl;
+    p.launches[g2d::KC_BAND_GEMM] += tasks;
+  }
   const int n = n_classes < g2d::KC_COUNT ? n_classes : g2d::KC_COUNT;
   for (int c = 0; c < n; ++c) {
     if (ms) ms[c] = p.ms[c];
@@ -311,8 +319,7 @@ int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* fl
 }
 
 const char* gptq2d_profile_class_name(int cls) {
-  static const char* names[g2d::KC_COUNT] = {"round", "near", "chol", "panel",
-                                             "trailing", "trtri", "other", "far"};
+  static const char* names[g2d::KC_COUNT] = {"sweep", "band_gemm", "chol", "trtri", "other"};
   return (cls >= 0 && cls < g2d::KC_COUNT) ? names[cls] : "unknown";
 }
 

@@ -9,19 +9,24 @@
 namespace g2d {
 
 enum KernelClass : int {
-  KC_ROUND = 0,     // anti-diagonal rounding of one block diagonal
-  KC_BAND = 1,      // near band feedback GEMMs of one block diagonal
-  KC_POTRF = 2,     // one Cholesky step: diagonal block + inverse, panel, trailing
-  KC_PANEL = 3,     // panel solve GEMM
-  KC_TRAILING = 4,  // trailing-update GEMM of the Cholesky
-  KC_TRTRI = 5,     // triangular-inverse doubling GEMMs
-  KC_OTHER = 6,     // reverse/finalize/init/check kernels
-  KC_FAR = 7,       // far band feedback GEMMs (second stream)
-  KC_COUNT = 8
+  KC_SWEEP = 0,      // the persistent sweep kernel: rounding, band updates, outputs
+  KC_BAND_GEMM = 1,  // band-update tasks inside the sweep (busy time of the workgroups
+                     // that ran them, in CU-milliseconds; one "launch" per task)
+  KC_POTRF = 2,      // one Cholesky step of the factor stage
+  KC_TRTRI = 3,      // triangular-inverse doubling GEMMs
+  KC_OTHER = 4,      // reverse/finalize/init/check kernels
+  KC_COUNT = 5
 };
 
 bool prof_on();
 void prof_begin(int cls, hipStream_t s);
 void prof_end(int cls, hipStream_t s, double flops, double bytes);
+
+// Device counters of the band-update tasks, accumulated by the sweep kernel while the
+// hook is on (nullptr otherwise): [0] busy wall-clock ticks (100 MHz) summed over tasks,
+// [1] task flops, [2] tasks.
+unsigned long long* band_stats_device();
+// Reads the counters into the class totals and clears them (synchronous).
+hipError_t band_stats_collect(double* cu_ms, double* flops, int64_t* tasks);
 
 }  // namespace g2d

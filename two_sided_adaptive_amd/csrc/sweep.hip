@@ -87,6 +87,7 @@ struct SweepArgs {
   int* vcnt;                 // [Mb * Nb] contributions applied to Vf, per 64 x 64 tile
   int* hcnt;                 // [Mb * Nb] contributions applied to Hf, per tile
   unsigned long long* qd;    // [total] task descriptors (0 = not yet published)
+  unsigned long long* stats; // band-update task accounting while profiling, else null
 };
 
 // ---------------------------------------------------------------------------
@@ -346,6 +347,7 @@ struct BandSmem {
   T g0s[4][MU][MU];        // per wave, skewed: g0s[r][sl] = (W - G outside)[r][(sl - r) % 16]
   T h0s[4][MU][MU];        // per wave, skewed: H from outside; scratch during a sweep
   int8_t zz[4][MU][MU];    // per wave: codes of the micro-tile
+  T sc[BB];                // the band's row scales (1 past the last row)
   int bcast[4];
 };
 
@@ -567,7 +569,6 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
   // R row-major and Delta transposed (read by other workgroups), codes and Q
   const rsrc_t rro = make_rsrc(a.R + o0, tile_bytes);
   const rsrc_t rdt = make_rsrc(a.DT + c0 * m + row0, ((int64_t)(nc - 1) * m + rows) * es);
-  const T* sc_base = a.s + row0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int c = cl, r = kq + 4 * u;  // consecutive lanes along a row
@@ -576,7 +577,7 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
       buf_store_dev<T>(sm.rT[s4][c][MU * w + r], rro, (uint32_t)(r * n + c));
       const int z = sm.zz[w][r][c];
       a.codes[o] = (int8_t)z;
-      a.Q[o] = sc_base[r] * T(z);
+      a.Q[o] = sm.sc[MU * w + r] * T(z);
     }
     const int r2 = cl, c2 = kq + 4 * u;  // consecutive lanes along a column
     if (r2 < rows && c2 < nc) buf_store_dev<T>(sm.dh[w][s8][r2][c2], rdt, (uint32_t)(c2 * m + r2));
@@ -652,6 +653,10 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
     const T sv0 = buf_load<T>(make_rsrc(a.s + r0, (int64_t)mr * es), (uint32_t)gr);
     const T s_r = rowok ? sv0 : T(1);
     const T rs_r = T(1) / s_r;
+    if (tid < BB) {
+      const T v = buf_load<T>(make_rsrc(a.s + r0, (int64_t)mr * es), (uint32_t)tid);
+      sm.sc[tid] = tid < mr ? v : T(1);
+    }
 
     const int nphase = a.Nj + nw - 1;
     for (int p = 0; p < nphase; ++p) {
@@ -922,6 +927,7 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
     const T* pb = dir == 0 ? a.R : a.DT;
     const int64_t ldb = dir == 0 ? n : m;
     T* pc = dir == 0 ? a.Vf + p0 * n + q0 : a.Hf + q0 * n + p0;
+    const long long t_begin = wall_clock64();
     if (far)
       panel_gemm<T, GOUT * BB / kKC>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n,
                                      PW, QW, ks, dir != 0, first, sm);
@@ -934,6 +940,11 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
       for (int t = t0; t <= t1; ++t) {
         int* cnt = dir == 0 ? a.vcnt + (int64_t)t * a.Nb + other : a.hcnt + (int64_t)other * a.Nb + t;
         st_dev(cnt, push_seq(t, own, far) + 1);
+      }
+      if (a.stats) {
+        atomicAdd(a.stats + 0, (unsigned long long)(wall_clock64() - t_begin));
+        atomicAdd(a.stats + 1, (unsigned long long)(2 * (int64_t)PW * QW * ks));
+        atomicAdd(a.stats + 2, 1ull);
       }
     }
   }
@@ -996,6 +1007,9 @@ SyncLayout sync_layout(int64_t m, int64_t n) {
   return s;
 }
 
+// band-update task accounting of the measurement hook (see prof.hpp)
+__device__ unsigned long long g_band_stats[3];
+
 template <typename T>
 hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, const T* Ub,
                        const T* scales, int8_t* codes, T* Q, void* ws, int* info, hipStream_t s) {
@@ -1034,6 +1048,7 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   a.codes = codes;
   a.Q = Q;
   a.info = info;
+  a.stats = band_stats_device();
 
   int dev = 0, ncu = 0, occ = 0;
   hipError_t e;
@@ -1066,13 +1081,33 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   const double fl = pr ? (double)m * (double)n * (double)(m + n - 2) : 0.0;
   const double by = pr ? es * (3.0 * (double)mn + (double)m * m + (double)n * n + (double)m) +
                              (double)mn : 0.0;
-  prof_begin(KC_ROUND, s);
+  prof_begin(KC_SWEEP, s);
   k_sweep<T><<<grid, kThreads, 0, s>>>(a);
-  prof_end(KC_ROUND, s, fl, by);
+  prof_end(KC_SWEEP, s, fl, by);
   return hipGetLastError();
 }
 
 }  // namespace
+
+unsigned long long* band_stats_device() {
+  if (!prof_on()) return nullptr;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_band_stats)) != hipSuccess) return nullptr;
+  return (unsigned long long*)p;
+}
+
+hipError_t band_stats_collect(double* cu_ms, double* flops, int64_t* tasks) {
+  unsigned long long h[3] = {0, 0, 0};
+  hipError_t e = hipMemcpyFromSymbol(h, HIP_SYMBOL(g_band_stats), sizeof(h), 0,
+                                     hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  const unsigned long long z[3] = {0, 0, 0};
+  e = hipMemcpyToSymbol(HIP_SYMBOL(g_band_stats), z, sizeof(z), 0, hipMemcpyHostToDevice);
+  *cu_ms = (double)h[0] * 1e-5;  // 100 MHz ticks -> ms
+  *flops = (double)h[1];
+  *tasks = (int64_t)h[2];
+  return e;
+}
 
 size_t sweep_workspace(int64_t m, int64_t n, int dtype) {
   const size_t es = dtype == 0 ? sizeof(float) : sizeof(double);
