@@ -57,9 +57,19 @@ constexpr int FAR_OFF = 1;  // far pushes of outer band O reach targets >= GOUT 
 constexpr int kPanel = 2;   // target blocks per GEMM task
 constexpr int kThreads = 256;
 constexpr int kSpinLimit = 1 << 22;
+constexpr int NXCD = 8;     // accelerator complex dies (XCDs) of the MI355X, one L2 each
 
-// control words at the start of the sync area
-enum Ctl : int { kBandCtr = 0, kHead = 1, kTail = 2, kAbort = 3, kTicket = 4, kCtlWords = 8 };
+// control words at the start of the sync area; the per-XCD words sit on their own
+// 128-byte lines
+enum Ctl : int {
+  kHead = 0,
+  kTail = 1,
+  kAbort = 3,
+  kLine = 32,                       // ints per 128-byte line
+  kBandX = kLine,                   // + kLine x: bands claimed by workgroups on XCD x
+  kXTicket = kLine * (1 + NXCD),    // + kLine x: workgroups started on XCD x
+  kCtlWords = kLine * (1 + 2 * NXCD)
+};
 
 // Cache policy of loads and stores that other workgroups of the same launch produce or
 // consume: device scope (sc1), so they bypass the non-coherent caches.
@@ -70,7 +80,8 @@ struct SweepArgs {
   int64_t m, n;
   int Mb, Nb, Nj, lo, hi, bits;
   int total;  // band-update tasks in the whole sweep
-  int nbw;    // band workers
+  int nbxcd;  // band workers per XCD
+  int gs;     // bands are dealt to the XCDs in groups of gs consecutive bands
   const T* Ua;
   const T* Ub;
   const T* s;
@@ -157,6 +168,8 @@ __device__ inline void st_dev(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline bool aborted(const int* ctl) { return ld_dev(ctl + kAbort) != 0; }
+// XCD (accelerator complex die) this wave runs on: hardware register XCC_ID
+__device__ inline int xcd_id() { return (int)__builtin_amdgcn_s_getreg((3 << 11) | 20) % NXCD; }
 __device__ inline void abort_sweep(int* ctl, int* info) {
   if (atomicCAS(ctl + kAbort, 0, 1) == 0) record_info(info, 4, 0);
 }
@@ -196,6 +209,20 @@ __device__ inline float buf_load_dev<float>(rsrc_t r, uint32_t elem) {
 template <>
 __device__ inline double buf_load_dev<double>(rsrc_t r, uint32_t elem) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, 0, kDev);
+  return __hiloint2double((int)v[1], (int)v[0]);
+}
+// Load that bypasses the CU's L1 but may hit the XCD's L2 (data stored through that L2
+// by a workgroup of the same XCD).
+constexpr int kL2 = 1;
+template <typename T>
+__device__ inline T buf_load_l2(rsrc_t r, uint32_t elem);
+template <>
+__device__ inline float buf_load_l2<float>(rsrc_t r, uint32_t elem) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, elem * 4u, 0, kL2));
+}
+template <>
+__device__ inline double buf_load_l2<double>(rsrc_t r, uint32_t elem) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, 0, kL2);
   return __hiloint2double((int)v[1], (int)v[0]);
 }
 template <typename T>
@@ -354,7 +381,7 @@ struct BandSmem {
 // Rounds micro-tile (w, j) of band K and stores its R, Delta, codes and Q.
 template <typename T>
 __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, int K, int w,
-                                        int j, int ev, const T (&aVn)[BB / 4],
+                                        int j, int ev, int& vblk, const T (&aVn)[BB / 4],
                                         const T (&aVi)[3 * MU / 4], const T (&cu)[4], T cup,
                                         T cup2, T s_r, T rs_r) {
   typedef typename Mfma<T>::acc_t acc_t;
@@ -373,36 +400,15 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
   const int s4 = j & 3, s8 = j & 7;
   const int64_t es = sizeof(T);
 
-  // dependencies: R of the band above for this micro-column; the pushed feedback of
-  // this 64-wide block
-  if (K > 0 && !wait_ge(a.rdone + K - 1, j + 1, a.ctl, a.info)) return;
-  if (ev > 0 && !wait_ge(a.vcnt + (int64_t)K * a.Nb + L, ev, a.ctl, a.info)) return;
-  if (eh > 0 && !wait_ge(a.hcnt + (int64_t)K * a.Nb + L, eh, a.ctl, a.info)) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-
-  // global loads (all in flight together)
+  // Loads are issued in the order they are consumed (the counter that tracks them
+  // retires in order): the U'b window and diagonal block and W first; then, once this
+  // 64-wide block's contribution counters are complete (checked once per block by each
+  // wave), the pushed feedback Vf / Hf; last the R of the band above, whose product is
+  // computed after the others so that its latency overlaps them.
   const int64_t row0 = r0 + MU * w;  // first row of this micro-tile
   const int rows = mr - MU * w;      // valid rows (1..16)
   const int64_t tile_bytes = ((int64_t)(rows - 1) * n + nc) * es;
   const int64_t o0 = row0 * n + c0;
-  const rsrc_t rw = make_rsrc(a.W + o0, tile_bytes);
-  const rsrc_t rvf = make_rsrc(a.Vf + o0, ev > 0 ? tile_bytes : 0);
-  const rsrc_t rhf = make_rsrc(a.Hf + o0, eh > 0 ? tile_bytes : 0);
-  T gin[4], hin[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t o = (uint32_t)(Mfma<T>::row(lane, e) * n + cl);
-    gin[e] = buf_load<T>(rw, o) - buf_load_dev<T>(rvf, o);
-    hin[e] = buf_load_dev<T>(rhf, o);
-  }
-  // R of the band above, column block of this micro-column (k-major B operand)
-  T bnb[BB / 4];
-  {
-    const rsrc_t rr = make_rsrc(K > 0 ? a.R + (r0 - BB) * n + c0 : a.R,
-                                K > 0 ? ((int64_t)(BB - 1) * n + nc) * es : 0);
-#pragma unroll
-    for (int s = 0; s < BB / 4; ++s) bnb[s] = buf_load_dev<T>(rr, (uint32_t)((4 * s + kq) * n + cl));
-  }
   // U'b rows of the local window, this micro-column's columns (k-major B operand)
   T bwin[7 * MU / 4];
   {
@@ -420,6 +426,47 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
     for (int u = 0; u < MU * MU / 64; ++u) {
       const int idx = lane + 64 * u, k = idx >> 4, c = idx & 15;
       ubd[u] = buf_load<T>(rb, (uint32_t)(k * n + c));
+    }
+  }
+  T gin[4], hin[4];
+  {
+    const rsrc_t rw = make_rsrc(a.W + o0, tile_bytes);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gin[e] = buf_load<T>(rw, (uint32_t)(Mfma<T>::row(lane, e) * n + cl));
+  }
+  if (vblk != L) {
+    if (ev > 0 && !wait_ge(a.vcnt + (int64_t)K * a.Nb + L, ev, a.ctl, a.info)) return;
+    if (eh > 0 && !wait_ge(a.hcnt + (int64_t)K * a.Nb + L, eh, a.ctl, a.info)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    vblk = L;
+  }
+  {
+    const rsrc_t rvf = make_rsrc(a.Vf + o0, ev > 0 ? tile_bytes : 0);
+    const rsrc_t rhf = make_rsrc(a.Hf + o0, eh > 0 ? tile_bytes : 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t o = (uint32_t)(Mfma<T>::row(lane, e) * n + cl);
+      gin[e] -= buf_load_dev<T>(rvf, o);
+      hin[e] = buf_load_dev<T>(rhf, o);
+    }
+  }
+  if (K > 0 && !wait_ge(a.rdone + K - 1, j + 1, a.ctl, a.info)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // R of the band above (k-major B operand).  When that band lives on this XCD its stores
+  // went through this L2, so the shared L2 serves it; otherwise it is read at device scope.
+  // Only in fp64: there a micro-tile row is one whole 128-byte line (n a multiple of 16
+  // and 16-element aligned rows), so no line holding it can have been cached before the
+  // band above wrote all of it; an fp32 row is half a line.
+  T bnb[BB / 4];
+  {
+    const rsrc_t rr = make_rsrc(K > 0 ? a.R + (r0 - BB) * n + c0 : a.R,
+                                K > 0 ? ((int64_t)(BB - 1) * n + nc) * es : 0);
+    if (sizeof(T) == 8 && n % MU == 0 && K % a.gs != 0) {
+#pragma unroll
+      for (int s = 0; s < BB / 4; ++s) bnb[s] = buf_load_l2<T>(rr, (uint32_t)((4 * s + kq) * n + cl));
+    } else {
+#pragma unroll
+      for (int s = 0; s < BB / 4; ++s) bnb[s] = buf_load_dev<T>(rr, (uint32_t)((4 * s + kq) * n + cl));
     }
   }
 
@@ -441,13 +488,6 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
   // feedback from outside the micro-tile (MFMA), two chains per product
   {
     acc_t v0 = acc_t{0, 0, 0, 0}, v1 = acc_t{0, 0, 0, 0};
-    if (K > 0) {
-#pragma unroll
-      for (int s = 0; s < BB / 4; s += 2) {
-        v0 = Mfma<T>::run(aVn[s], bnb[s], v0);
-        v1 = Mfma<T>::run(aVn[s + 1], bnb[s + 1], v1);
-      }
-    }
     // earlier micro-rows of this band, same micro-column (written in earlier phases)
 #pragma unroll
     for (int s = 0; s < 3 * MU / 4; s += 2) {
@@ -464,6 +504,14 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
         const int k0 = 4 * s + kq, k1 = 4 * s + 4 + kq;
         h0 = Mfma<T>::run(sm.dh[w][(clo + (k0 >> 4)) & 7][cl][k0 & 15], bwin[s], h0);
         h1 = Mfma<T>::run(sm.dh[w][(clo + (k1 >> 4)) & 7][cl][k1 & 15], bwin[s + 1], h1);
+      }
+    }
+    // the band above last: its loads were issued last
+    if (K > 0) {
+#pragma unroll
+      for (int s = 0; s < BB / 4; s += 2) {
+        v0 = Mfma<T>::run(aVn[s], bnb[s], v0);
+        v1 = Mfma<T>::run(aVn[s + 1], bnb[s + 1], v1);
       }
     }
 #pragma unroll
@@ -615,7 +663,16 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
   const int64_t es = sizeof(T);
   for (;;) {
     __syncthreads();
-    if (tid == 0) sm.bcast[0] = aborted(a.ctl) ? a.Mb : atomicAdd(a.ctl + kBandCtr, 1);
+    // bands go to the XCDs in groups of gs consecutive bands, so a band usually has the
+    // band above it on its own XCD and reads its R from the shared L2
+    if (tid == 0) {
+      int K = a.Mb;
+      if (!aborted(a.ctl)) {
+        const int x = xcd_id(), c = atomicAdd(a.ctl + kBandX + kLine * x, 1);
+        K = a.gs * (x + NXCD * (c / a.gs)) + c % a.gs;
+      }
+      sm.bcast[0] = K < a.Mb ? K : a.Mb;
+    }
     __syncthreads();
     const int K = sm.bcast[0];
     if (K >= a.Mb) return;
@@ -659,6 +716,7 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
     }
 
     const int nphase = a.Nj + nw - 1;
+    int vblk = -1;  // last 64-wide block whose contribution counters this wave checked
     for (int p = 0; p < nphase; ++p) {
       const int cdone = p - (nw - 1);  // micro-column completed by this phase
       const bool closes = cdone >= 0 && ((cdone & 3) == 3 || cdone == a.Nj - 1);
@@ -667,7 +725,7 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
         base = atomicAdd(a.ctl + kTail, block_task_count(K, cdone / GOUT, a.Mb, a.Nb));
       const int j = p - w;
       if (w < nw && j >= 0 && j < a.Nj && !aborted(a.ctl))
-        round_micro_tile<T>(a, sm, K, w, j, ev, aVn, aVi, cu, cup, cup2, s_r, rs_r);
+        round_micro_tile<T>(a, sm, K, w, j, ev, vblk, aVn, aVi, cu, cup, cup2, s_r, rs_r);
       drain();
       __syncthreads();
       if (tid == 0 && cdone >= 0 && !aborted(a.ctl)) {
@@ -956,18 +1014,18 @@ struct SweepSmem {
   static constexpr size_t kBytes = kBand > kGemm ? kBand : kGemm;
 };
 
-// The persistent sweep: workgroups draw a ticket when they start; ticket 0 and tickets
-// beyond the band workers take band-update tasks, the others own bands (and take tasks
-// once no band is left).  Ticket 0 being a GEMM worker guarantees that tasks make
-// progress however many workgroups are resident.
+// The persistent sweep.  Workgroups draw a ticket on their XCD when they start: ticket 0
+// of every XCD and tickets beyond nbxcd take band-update tasks (so tasks make progress
+// however many workgroups are resident), the others own bands of their XCD and take tasks
+// once no band is left.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_sweep(SweepArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[SweepSmem<T>::kBytes];
   __shared__ int ticket;
-  if (threadIdx.x == 0) ticket = atomicAdd(a.ctl + kTicket, 1);
+  if (threadIdx.x == 0) ticket = atomicAdd(a.ctl + kXTicket + kLine * xcd_id(), 1);
   __syncthreads();
   const int tk = ticket;
-  if (tk >= 1 && tk <= a.nbw) band_worker<T>(a, *reinterpret_cast<BandSmem<T>*>(smem));
+  if (tk >= 1 && tk <= a.nbxcd) band_worker<T>(a, *reinterpret_cast<BandSmem<T>*>(smem));
   gemm_worker<T>(a, *reinterpret_cast<GemmSmem<T>*>(smem));
 }
 
@@ -1066,7 +1124,11 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   if (nbw > a.Mb) nbw = a.Mb;
   if (nbw > grid / 2) nbw = grid / 2;
   if (nbw < 1) nbw = 1;
-  a.nbw = nbw;
+  // groups of up to eight consecutive bands per XCD, so that every XCD gets bands; one
+  // spare band worker per XCD
+  a.gs = (a.Mb + NXCD - 1) / NXCD < 8 ? (a.Mb + NXCD - 1) / NXCD : 8;
+  a.nbxcd = (nbw + NXCD - 1) / NXCD + 1;
+  if (a.nbxcd > grid / NXCD - 1) a.nbxcd = grid / NXCD - 1 > 0 ? grid / NXCD - 1 : 1;
 
   const bool pr = prof_on();
   const double es = (double)sizeof(T);
