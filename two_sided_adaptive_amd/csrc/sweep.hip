@@ -27,16 +27,16 @@
 //         counter of the band above;
 //       - from the band's own micro-columns in the current and the previous column
 //         block: MFMA products from the band's Delta history in LDS;
-//       - from everything further away: the accumulated buffers Vf (vertical) and Hf
-//         (horizontal), filled by GEMM workers.
+//       - from everything further away: accumulated vertical and horizontal feedback
+//         buffers, filled by GEMM workers (one pair per class of task, below).
 //     Consecutive bands therefore run one micro-column phase apart per wave: the
 //     wavefront of the whole matrix advances one micro-tile anti-diagonal at a time.
-//   * GEMM workers take band-update tasks from a queue that band workers fill when
-//     they complete a 64 x 64 block: 64 deep from one band (block) to the targets up to
-//     the first block of the next outer block, and, when the block closes an outer
-//     block, 256 deep from the whole outer block to every target beyond.  The
-//     contributions to one target tile are applied in the order of their sources, so
-//     the result is deterministic.
+//   * GEMM workers take band-update tasks from two queues that band workers fill when
+//     they complete a 64 x 64 block: near tasks, 64 deep from one band (block) to the
+//     targets up to the first block of the next outer block, and, when the block closes
+//     an outer block, far tasks, 256 deep from the whole outer block to every target
+//     beyond.  Within each class the contributions to one target tile are applied in
+//     the order of their sources, so the result is deterministic.
 // Every wait is bounded; a timeout aborts the sweep and reports info[0] = 4.
 #include <math.h>
 
@@ -53,7 +53,9 @@ namespace {
 constexpr int BB = 64;      // band height = block edge
 constexpr int MU = 16;      // micro-tile edge
 constexpr int GOUT = 4;     // bands (blocks) per outer band (block)
-constexpr int FAR_OFF = 1;  // far pushes of outer band O reach targets >= GOUT (O + 1) + FAR_OFF
+// far pushes of outer band (block) O reach targets >= GOUT (O + 1) + FAR_OFF; with an
+// offset of 2 a 256-deep task has a few phases to finish before its target needs it
+constexpr int FAR_OFF = 2;
 constexpr int kPanel = 2;   // target blocks per GEMM task
 constexpr int kThreads = 256;
 constexpr int kSpinLimit = 1 << 22;
@@ -62,14 +64,20 @@ constexpr int NXCD = 8;     // accelerator complex dies (XCDs) of the MI355X, on
 // control words at the start of the sync area; the per-XCD words sit on their own
 // 128-byte lines
 enum Ctl : int {
-  kHead = 0,
-  kTail = 1,
-  kAbort = 3,
+  kAbort = 0,
   kLine = 32,                       // ints per 128-byte line
-  kBandX = kLine,                   // + kLine x: bands claimed by workgroups on XCD x
-  kXTicket = kLine * (1 + NXCD),    // + kLine x: workgroups started on XCD x
-  kCtlWords = kLine * (1 + 2 * NXCD)
+  kHead = kLine,                    // + kLine c: next slot of queue c to claim
+  kTail = kLine * 3,                // + kLine c: slots of queue c reserved by producers
+  kBandX = kLine * 5,               // + kLine x: bands claimed by workgroups on XCD x
+  kXTicket = kLine * (5 + NXCD),    // + kLine x: workgroups started on XCD x
+  kCtlWords = kLine * (5 + 2 * NXCD)
 };
+// Band-update contributions come in two classes, each with its own accumulators,
+// contribution counters and task queue: near (64 deep, from the last few bands / blocks,
+// needed soon) and far (256 deep, from whole outer bands / blocks, needed later).  A
+// contribution only ever waits for earlier contributions of its own class, so each queue
+// is served in FIFO order by its own workers and near tasks never wait behind far ones.
+enum PushClass : int { kNear = 0, kFar = 1 };
 
 // Cache policy of loads and stores that other workgroups of the same launch produce or
 // consume: device scope (sc1), so they bypass the non-coherent caches.
@@ -79,15 +87,15 @@ template <typename T>
 struct SweepArgs {
   int64_t m, n;
   int Mb, Nb, Nj, lo, hi, bits;
-  int total;  // band-update tasks in the whole sweep
+  int qcap[2]; // band-update tasks of each class in the whole sweep
   int nbxcd;  // band workers per XCD
   int gs;     // bands are dealt to the XCDs in groups of gs consecutive bands
   const T* Ua;
   const T* Ub;
   const T* s;
   const T* W;
-  T* Vf;   // vertical feedback pushed by GEMM workers (subtracted from W)
-  T* Hf;   // horizontal feedback pushed by GEMM workers
+  T* Vacc[2];  // vertical feedback pushed by GEMM workers (subtracted from W), per class
+  T* Hacc[2];  // horizontal feedback pushed by GEMM workers, per class
   T* R;    // vertical residual, row-major m x n
   T* DT;   // Delta transposed, n x m
   int8_t* codes;
@@ -95,9 +103,9 @@ struct SweepArgs {
   int* info;
   int* ctl;                  // kCtlWords control words
   int* rdone;                // [Mb] micro-columns of each band whose R is stored
-  int* vcnt;                 // [Mb * Nb] contributions applied to Vf, per 64 x 64 tile
-  int* hcnt;                 // [Mb * Nb] contributions applied to Hf, per tile
-  unsigned long long* qd;    // [total] task descriptors (0 = not yet published)
+  int* vcnt[2];              // [Mb * Nb] per class: contributions applied, per 64 x 64 tile
+  int* hcnt[2];              // [Mb * Nb] per class, horizontal
+  unsigned long long* qd[2]; // [qcap] per class: task descriptors (0 = not yet published)
   unsigned long long* stats; // band-update task accounting while profiling, else null
 };
 
@@ -107,17 +115,19 @@ struct SweepArgs {
 // Source index `own` (a band for vertical pushes, a column block for horizontal ones)
 // pushes 64 deep to targets [own + 2, GOUT (own / GOUT) + GOUT - 1 + FAR_OFF]; the last
 // band of an outer band pushes the whole outer band, 256 deep, to every target from
-// GOUT (own / GOUT + 1) + FAR_OFF on.  Target T thus receives, in source order, the far
-// pushes of outer bands 0 .. nfar(T) - 1 and then the near pushes of the bands
-// GOUT nfar(T) .. T - 2; band T - 1 is applied by the band worker itself.
+// GOUT (own / GOUT + 1) + FAR_OFF on (FAR_OFF >= 1).  Target T thus receives, in
+// source order, the far pushes of outer bands 0 .. nfar(T) - 1 and then the near pushes
+// of the bands GOUT nfar(T) .. T - 2; band T - 1 is applied by the band worker itself.
 __host__ __device__ inline int nfar(int T) {
   return T >= GOUT + FAR_OFF ? (T - GOUT - FAR_OFF) / GOUT + 1 : 0;
 }
-__host__ __device__ inline int expected_pushes(int T) {
-  return T >= 2 ? T - 1 - (GOUT - 1) * nfar(T) : 0;
+// contributions of one class that target T receives, and a contribution's rank in them
+__host__ __device__ inline int expected_class(int T, int cls) {
+  const int nf = nfar(T);
+  return cls == kFar ? nf : (T >= 2 ? T - 1 - GOUT * nf : 0);
 }
 __host__ __device__ inline int push_seq(int T, int own, bool far) {
-  return far ? own / GOUT : nfar(T) + (own - GOUT * nfar(T));
+  return far ? own / GOUT : own - GOUT * nfar(T);
 }
 __host__ __device__ inline void near_range(int own, int nt, int* t0, int* t1) {
   *t0 = own + 2;
@@ -136,16 +146,19 @@ __host__ __device__ inline void far_range(int own, int nt, int* t0, int* t1) {
 __host__ __device__ inline int npanels(int t0, int t1) {
   return t1 >= t0 ? (t1 - t0) / kPanel + 1 : 0;
 }
-__host__ __device__ inline int block_task_count(int K, int L, int Mb, int Nb) {
+__host__ __device__ inline int block_task_count(int K, int L, int Mb, int Nb, int cls) {
   int t0, t1, c = 0;
-  near_range(K, Mb, &t0, &t1);
-  c += npanels(t0, t1);
-  near_range(L, Nb, &t0, &t1);
-  c += npanels(t0, t1);
-  far_range(K, Mb, &t0, &t1);
-  c += npanels(t0, t1);
-  far_range(L, Nb, &t0, &t1);
-  c += npanels(t0, t1);
+  if (cls == kNear) {
+    near_range(K, Mb, &t0, &t1);
+    c += npanels(t0, t1);
+    near_range(L, Nb, &t0, &t1);
+    c += npanels(t0, t1);
+  } else {
+    far_range(K, Mb, &t0, &t1);
+    c += npanels(t0, t1);
+    far_range(L, Nb, &t0, &t1);
+    c += npanels(t0, t1);
+  }
   return c;
 }
 
@@ -381,7 +394,7 @@ struct BandSmem {
 // Rounds micro-tile (w, j) of band K and stores its R, Delta, codes and Q.
 template <typename T>
 __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, int K, int w,
-                                        int j, int ev, int& vblk, const T (&aVn)[BB / 4],
+                                        int j, int& vblk, const T (&aVn)[BB / 4],
                                         const T (&aVi)[3 * MU / 4], const T (&cu)[4], T cup,
                                         T cup2, T s_r, T rs_r) {
   typedef typename Mfma<T>::acc_t acc_t;
@@ -394,7 +407,6 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
   const int64_t c0 = (int64_t)j * MU;
   const int nc = (n - c0) < MU ? (int)(n - c0) : MU;
   const int L = j / GOUT;  // 64-wide column block
-  const int eh = expected_pushes(L);
   const int clo = GOUT * (L > 0 ? L - 1 : 0);  // first micro-column of the local window
   const int nwin = j - clo;                     // window micro-columns, 0..7
   const int s4 = j & 3, s8 = j & 7;
@@ -403,7 +415,7 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
   // Loads are issued in the order they are consumed (the counter that tracks them
   // retires in order): the U'b window and diagonal block and W first; then, once this
   // 64-wide block's contribution counters are complete (checked once per block by each
-  // wave), the pushed feedback Vf / Hf; last the R of the band above, whose product is
+  // wave), the pushed feedback of both classes; last the R of the band above, whose product is
   // computed after the others so that its latency overlaps them.
   const int64_t row0 = r0 + MU * w;  // first row of this micro-tile
   const int rows = mr - MU * w;      // valid rows (1..16)
@@ -435,19 +447,29 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
     for (int e = 0; e < 4; ++e) gin[e] = buf_load<T>(rw, (uint32_t)(Mfma<T>::row(lane, e) * n + cl));
   }
   if (vblk != L) {
-    if (ev > 0 && !wait_ge(a.vcnt + (int64_t)K * a.Nb + L, ev, a.ctl, a.info)) return;
-    if (eh > 0 && !wait_ge(a.hcnt + (int64_t)K * a.Nb + L, eh, a.ctl, a.info)) return;
+    const int64_t tile = (int64_t)K * a.Nb + L;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int evc = expected_class(K, c), ehc = expected_class(L, c);
+      if (evc > 0 && !wait_ge(a.vcnt[c] + tile, evc, a.ctl, a.info)) return;
+      if (ehc > 0 && !wait_ge(a.hcnt[c] + tile, ehc, a.ctl, a.info)) return;
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     vblk = L;
   }
-  {
-    const rsrc_t rvf = make_rsrc(a.Vf + o0, ev > 0 ? tile_bytes : 0);
-    const rsrc_t rhf = make_rsrc(a.Hf + o0, eh > 0 ? tile_bytes : 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hin[e] = T(0);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const rsrc_t rvf =
+        make_rsrc(a.Vacc[c] + o0, expected_class(K, c) > 0 ? tile_bytes : 0);
+    const rsrc_t rhf =
+        make_rsrc(a.Hacc[c] + o0, expected_class(L, c) > 0 ? tile_bytes : 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t o = (uint32_t)(Mfma<T>::row(lane, e) * n + cl);
       gin[e] -= buf_load_dev<T>(rvf, o);
-      hin[e] = buf_load_dev<T>(rhf, o);
+      hin[e] += buf_load_dev<T>(rhf, o);
     }
   }
   if (K > 0 && !wait_ge(a.rdone + K - 1, j + 1, a.ctl, a.info)) return;
@@ -632,25 +654,35 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
   }
 }
 
-// Publishes the band-update tasks of completed block (K, L) into slots base...
+// Publishes the band-update tasks of completed block (K, L): near tasks into queue slots
+// base_near..., far tasks into base_far...; within a class vertical panels come first.
+// The lanes of one wave write the descriptors in parallel.
 template <typename T>
-__device__ inline void publish_block(const SweepArgs<T>& a, int K, int L, int base) {
-  int slot = base;
-  int t0, t1;
-  // near pushes first (their targets are closest), then far pushes
-  for (int far = 0; far < 2; ++far)
-    for (int dir = 0; dir < 2; ++dir) {
-      const int own = dir == 0 ? K : L, other = dir == 0 ? L : K;
-      const int nt = dir == 0 ? a.Mb : a.Nb;
-      if (far) far_range(own, nt, &t0, &t1);
-      else near_range(own, nt, &t0, &t1);
-      for (int p0 = t0; p0 <= t1; p0 += kPanel) {
-        const int p1 = p0 + kPanel - 1 < t1 ? p0 + kPanel - 1 : t1;
-        __hip_atomic_store(a.qd + slot, pack_task(far != 0, dir, own, other, p0, p1),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ++slot;
-      }
-    }
+__device__ inline void publish_block(const SweepArgs<T>& a, int K, int L, int base_near,
+                                     int base_far, int lane) {
+  int nv0, nv1, nh0, nh1, fv0, fv1, fh0, fh1;
+  near_range(K, a.Mb, &nv0, &nv1);
+  near_range(L, a.Nb, &nh0, &nh1);
+  far_range(K, a.Mb, &fv0, &fv1);
+  far_range(L, a.Nb, &fh0, &fh1);
+  const int nnv = npanels(nv0, nv1), nnh = npanels(nh0, nh1);
+  const int nfv = npanels(fv0, fv1), nfh = npanels(fh0, fh1);
+  const int nn = nnv + nnh, total = nn + nfv + nfh;
+  for (int i = lane; i < total; i += 64) {
+    const bool far = i >= nn;
+    const int k = far ? i - nn : i;  // index within the class
+    const int nvc = far ? nfv : nnv;
+    const int dir = k >= nvc ? 1 : 0;
+    const int pi = dir ? k - nvc : k;
+    const int t0 = far ? (dir ? fh0 : fv0) : (dir ? nh0 : nv0);
+    const int t1 = far ? (dir ? fh1 : fv1) : (dir ? nh1 : nv1);
+    const int p0 = t0 + kPanel * pi;
+    const int p1 = p0 + kPanel - 1 < t1 ? p0 + kPanel - 1 : t1;
+    const int own = dir == 0 ? K : L, other = dir == 0 ? L : K;
+    __hip_atomic_store((far ? a.qd[kFar] + base_far : a.qd[kNear] + base_near) + k,
+                       pack_task(far, dir, own, other, p0, p1), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <typename T>
@@ -679,7 +711,6 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
     const int64_t r0 = (int64_t)K * BB;
     const int mr = (m - r0) < BB ? (int)(m - r0) : BB;
     const int nw = (mr + MU - 1) / MU;  // waves with rows
-    const int ev = expected_pushes(K);
     // band constants of this wave: U'a blocks as MFMA A fragments, in-micro-tile
     // vertical coefficients, the row's scale
     // U'a rows of the band above and of this band, columns of this band
@@ -720,17 +751,26 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
     for (int p = 0; p < nphase; ++p) {
       const int cdone = p - (nw - 1);  // micro-column completed by this phase
       const bool closes = cdone >= 0 && ((cdone & 3) == 3 || cdone == a.Nj - 1);
+      // The trailing wave (it completes the block) reserves the block's queue slots at
+      // the start of the phase, lane c for queue c; the returned bases are first needed
+      // after the phase, so the atomics' latency overlaps the phase's work.
+      const bool pub = w == nw - 1;
       int base = 0;
-      if (tid == 0 && closes)
-        base = atomicAdd(a.ctl + kTail, block_task_count(K, cdone / GOUT, a.Mb, a.Nb));
+      if (pub && closes && lane < 2) {
+        const int cnt = block_task_count(K, cdone / GOUT, a.Mb, a.Nb, lane);
+        if (cnt > 0) base = atomicAdd(a.ctl + kTail + kLine * lane, cnt);
+      }
       const int j = p - w;
-      if (w < nw && j >= 0 && j < a.Nj && !aborted(a.ctl))
-        round_micro_tile<T>(a, sm, K, w, j, ev, vblk, aVn, aVi, cu, cup, cup2, s_r, rs_r);
+      // (after an abort every wait inside returns at once, so the band drains quickly)
+      if (w < nw && j >= 0 && j < a.Nj)
+        round_micro_tile<T>(a, sm, K, w, j, vblk, aVn, aVi, cu, cup, cup2, s_r, rs_r);
       drain();
       __syncthreads();
-      if (tid == 0 && cdone >= 0 && !aborted(a.ctl)) {
-        if (closes) publish_block(a, K, cdone / GOUT, base);
-        st_dev(a.rdone + K, cdone + 1);
+      if (pub && cdone >= 0) {
+        if (closes)
+          publish_block(a, K, cdone / GOUT, __builtin_amdgcn_readlane(base, kNear),
+                        __builtin_amdgcn_readlane(base, kFar), lane);
+        if (lane == 0) st_dev(a.rdone + K, cdone + 1);
       }
     }
   }
@@ -907,7 +947,7 @@ __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t l
 }
 
 template <typename T>
-__device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
+__device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm, int cls) {
   const int64_t m = a.m, n = a.n;
   const int tid = threadIdx.x;
   for (;;) {
@@ -915,12 +955,12 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
     if (tid < 64) {
       // claim the next task and wait for its descriptor (whole first wave)
       int slot = 0;
-      if (tid == 0) slot = aborted(a.ctl) ? a.total : atomicAdd(a.ctl + kHead, 1);
+      if (tid == 0) slot = aborted(a.ctl) ? a.qcap[cls] : atomicAdd(a.ctl + kHead + kLine * cls, 1);
       slot = __builtin_amdgcn_readfirstlane(slot);
       unsigned long long d = 0;
-      if (slot < a.total) {
+      if (slot < a.qcap[cls]) {
         for (int it = 0;; ++it) {
-          d = __hip_atomic_load(a.qd + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          d = __hip_atomic_load(a.qd[cls] + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           d = ((unsigned long long)__builtin_amdgcn_readfirstlane((int)(d >> 32)) << 32) |
               (unsigned)__builtin_amdgcn_readfirstlane((int)d);
           if (d >> 63) break;
@@ -945,7 +985,8 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
         bool ok = true;
         for (int t = t0; t <= t1 && ok; ++t) {
           const int seq = push_seq(t, own, far);
-          int* cnt = dir == 0 ? a.vcnt + (int64_t)t * a.Nb + other : a.hcnt + (int64_t)other * a.Nb + t;
+          int* cnt = dir == 0 ? a.vcnt[cls] + (int64_t)t * a.Nb + other
+                              : a.hcnt[cls] + (int64_t)other * a.Nb + t;
           ok = wait_ge(cnt, seq, a.ctl, a.info);
           if (seq == 0) first |= 1 << (t - t0);
         }
@@ -960,7 +1001,7 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
     }
     __syncthreads();
     const unsigned long long d = sm.desc;
-    if (sm.bcast[0] >= a.total) return;
+    if (sm.bcast[0] >= a.qcap[cls]) return;
     if (!(d >> 63)) {
       if (aborted(a.ctl)) return;
       continue;
@@ -976,15 +1017,15 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
     const int64_t p0 = (int64_t)t0 * BB;
     const int64_t pend = (int64_t)(t1 + 1) * BB < ext ? (int64_t)(t1 + 1) * BB : ext;
     const int PW = (int)(pend - p0);
-    // vertical: Vf[p0 + x][q0 + y] += sum_k U'a[src0 + k][p0 + x] R[src0 + k][q0 + y];
-    // horizontal: Hf[q0 + y][p0 + x] += sum_k U'b[src0 + k][p0 + x] Delta^T[src0 + k][q0 + y]
+    // vertical: V[p0 + x][q0 + y] += sum_k U'a[src0 + k][p0 + x] R[src0 + k][q0 + y];
+    // horizontal: H[q0 + y][p0 + x] += sum_k U'b[src0 + k][p0 + x] Delta^T[src0 + k][q0 + y]
     const int64_t q0 = (int64_t)other * BB;
     const int64_t qext = dir == 0 ? n : m;
     const int QW = (qext - q0) < BB ? (int)(qext - q0) : BB;
     const T* pa = dir == 0 ? a.Ua : a.Ub;
     const T* pb = dir == 0 ? a.R : a.DT;
     const int64_t ldb = dir == 0 ? n : m;
-    T* pc = dir == 0 ? a.Vf + p0 * n + q0 : a.Hf + q0 * n + p0;
+    T* pc = dir == 0 ? a.Vacc[cls] + p0 * n + q0 : a.Hacc[cls] + q0 * n + p0;
     const long long t_begin = wall_clock64();
     if (far)
       panel_gemm<T, GOUT * BB / kKC>(pa + src0 * ext + p0, ext, pb + src0 * ldb + q0, ldb, pc, n,
@@ -996,7 +1037,8 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm) {
     __syncthreads();
     if (tid == 0) {
       for (int t = t0; t <= t1; ++t) {
-        int* cnt = dir == 0 ? a.vcnt + (int64_t)t * a.Nb + other : a.hcnt + (int64_t)other * a.Nb + t;
+        int* cnt = dir == 0 ? a.vcnt[cls] + (int64_t)t * a.Nb + other
+                            : a.hcnt[cls] + (int64_t)other * a.Nb + t;
         st_dev(cnt, push_seq(t, own, far) + 1);
       }
       if (a.stats) {
@@ -1015,9 +1057,10 @@ struct SweepSmem {
 };
 
 // The persistent sweep.  Workgroups draw a ticket on their XCD when they start: ticket 0
-// of every XCD and tickets beyond nbxcd take band-update tasks (so tasks make progress
-// however many workgroups are resident), the others own bands of their XCD and take tasks
-// once no band is left.
+// of every XCD takes far band-update tasks and ticket 1 near ones (so both queues make
+// progress however many workgroups are resident), tickets 2 .. nbxcd + 1 own bands of
+// their XCD and take far tasks once no band is left, and of the rest one in four takes
+// near tasks and three far ones.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_sweep(SweepArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[SweepSmem<T>::kBytes];
@@ -1025,8 +1068,9 @@ __global__ __launch_bounds__(kThreads) void k_sweep(SweepArgs<T> a) {
   if (threadIdx.x == 0) ticket = atomicAdd(a.ctl + kXTicket + kLine * xcd_id(), 1);
   __syncthreads();
   const int tk = ticket;
-  if (tk >= 1 && tk <= a.nbxcd) band_worker<T>(a, *reinterpret_cast<BandSmem<T>*>(smem));
-  gemm_worker<T>(a, *reinterpret_cast<GemmSmem<T>*>(smem));
+  if (tk >= 2 && tk < 2 + a.nbxcd) band_worker<T>(a, *reinterpret_cast<BandSmem<T>*>(smem));
+  const int cls = (tk == 1 || (tk >= 2 + a.nbxcd && tk % 4 == 0)) ? kNear : kFar;
+  gemm_worker<T>(a, *reinterpret_cast<GemmSmem<T>*>(smem), cls);
 }
 
 // control words, progress counters and task descriptors start at zero
@@ -1046,22 +1090,24 @@ __global__ __launch_bounds__(256) void k_check_scales(int64_t m, const T* __rest
 }
 
 struct SyncLayout {
-  int64_t ctl, rdone, vcnt, hcnt, qd, words;  // offsets in ints; qd 8-byte aligned
-  int total;
+  int64_t ctl, rdone, cnt, qd[2], words;  // offsets in ints; qd 8-byte aligned
+  int qcap[2];
 };
 SyncLayout sync_layout(int64_t m, int64_t n) {
   const int Mb = (int)cdiv(m, BB), Nb = (int)cdiv(n, BB);
-  int64_t total = 0;
+  int64_t cap[2] = {0, 0};
   for (int K = 0; K < Mb; ++K)
-    for (int L = 0; L < Nb; ++L) total += block_task_count(K, L, Mb, Nb);
+    for (int L = 0; L < Nb; ++L)
+      for (int c = 0; c < 2; ++c) cap[c] += block_task_count(K, L, Mb, Nb, c);
   SyncLayout s;
   s.ctl = 0;
   s.rdone = kCtlWords;
-  s.vcnt = s.rdone + Mb;
-  s.hcnt = s.vcnt + (int64_t)Mb * Nb;
-  s.qd = (s.hcnt + (int64_t)Mb * Nb + 1) / 2 * 2;
-  s.words = s.qd + 2 * total;
-  s.total = (int)total;
+  s.cnt = s.rdone + Mb;  // vcnt[near], vcnt[far], hcnt[near], hcnt[far]
+  s.qd[0] = (s.cnt + 4 * (int64_t)Mb * Nb + 1) / 2 * 2;
+  s.qd[1] = s.qd[0] + 2 * cap[0];
+  s.words = s.qd[1] + 2 * cap[1];
+  s.qcap[0] = (int)cap[0];
+  s.qcap[1] = (int)cap[1];
   return s;
 }
 
@@ -1091,18 +1137,22 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   a.Ub = Ub;
   a.s = scales;
   a.W = W;
-  a.Vf = take();
-  a.Hf = take();
+  a.Vacc[kNear] = take();
+  a.Vacc[kFar] = take();
+  a.Hacc[kNear] = take();
+  a.Hacc[kFar] = take();
   a.R = take();
   a.DT = take();
   const SyncLayout sl = sync_layout(m, n);
   int* sync = (int*)c;
   a.ctl = sync + sl.ctl;
   a.rdone = sync + sl.rdone;
-  a.vcnt = sync + sl.vcnt;
-  a.hcnt = sync + sl.hcnt;
-  a.qd = (unsigned long long*)(sync + sl.qd);
-  a.total = sl.total;
+  for (int c = 0; c < 2; ++c) {
+    a.vcnt[c] = sync + sl.cnt + (int64_t)c * a.Mb * a.Nb;
+    a.hcnt[c] = sync + sl.cnt + (int64_t)(2 + c) * a.Mb * a.Nb;
+    a.qd[c] = (unsigned long long*)(sync + sl.qd[c]);
+    a.qcap[c] = sl.qcap[c];
+  }
   a.codes = codes;
   a.Q = Q;
   a.info = info;
@@ -1125,10 +1175,11 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   if (nbw > grid / 2) nbw = grid / 2;
   if (nbw < 1) nbw = 1;
   // groups of up to eight consecutive bands per XCD, so that every XCD gets bands; one
-  // spare band worker per XCD
+  // spare band worker per XCD, and two workgroups per XCD left for the two task queues
   a.gs = (a.Mb + NXCD - 1) / NXCD < 8 ? (a.Mb + NXCD - 1) / NXCD : 8;
   a.nbxcd = (nbw + NXCD - 1) / NXCD + 1;
-  if (a.nbxcd > grid / NXCD - 1) a.nbxcd = grid / NXCD - 1 > 0 ? grid / NXCD - 1 : 1;
+  if (a.nbxcd > grid / NXCD - 2) a.nbxcd = grid / NXCD - 2;
+  if (a.nbxcd < 1 || grid < 3 * NXCD) return hipErrorInvalidConfiguration;
 
   const bool pr = prof_on();
   const double es = (double)sizeof(T);
@@ -1174,7 +1225,7 @@ hipError_t band_stats_collect(double* cu_ms, double* flops, int64_t* tasks) {
 size_t sweep_workspace(int64_t m, int64_t n, int dtype) {
   const size_t es = dtype == 0 ? sizeof(float) : sizeof(double);
   const SyncLayout sl = sync_layout(m, n);
-  return 4 * align_up((size_t)m * n * es) + align_up((size_t)sl.words * sizeof(int));
+  return 6 * align_up((size_t)m * n * es) + align_up((size_t)sl.words * sizeof(int));
 }
 
 hipError_t sweep_enqueue(int64_t m, int64_t n, int bits, int dtype, const void* W,
