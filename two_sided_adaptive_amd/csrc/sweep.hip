@@ -67,17 +67,21 @@ enum Ctl : int {
   kAbort = 0,
   kLine = 32,                       // ints per 128-byte line
   kHead = kLine,                    // + kLine c: next slot of queue c to claim
-  kTail = kLine * 3,                // + kLine c: slots of queue c reserved by producers
-  kBandX = kLine * 5,               // + kLine x: bands claimed by workgroups on XCD x
-  kXTicket = kLine * (5 + NXCD),    // + kLine x: workgroups started on XCD x
-  kCtlWords = kLine * (5 + 2 * NXCD)
+  kTail = kLine * 4,                // + kLine c: slots of queue c reserved by producers
+  kBandX = kLine * 7,               // + kLine x: bands claimed by workgroups on XCD x
+  kXTicket = kLine * (7 + NXCD),    // + kLine x: workgroups started on XCD x
+  kCtlWords = kLine * (7 + 2 * NXCD)
 };
-// Band-update contributions come in two classes, each with its own accumulators,
-// contribution counters and task queue: near (64 deep, from the last few bands / blocks,
-// needed soon) and far (256 deep, from whole outer bands / blocks, needed later).  A
-// contribution only ever waits for earlier contributions of its own class, so each queue
-// is served in FIFO order by its own workers and near tasks never wait behind far ones.
-enum PushClass : int { kNear = 0, kFar = 1 };
+// Band-update contributions come in three classes, each with its own accumulators,
+// contribution counters, task queue and workers:
+//   near: 64 deep, from the last few bands / blocks before the target;
+//   next: 256 deep, from the last outer band / block to the first kPanel targets it
+//         reaches (the far contribution that is needed soonest after it is published);
+//   far:  256 deep, every other contribution of whole outer bands / blocks.
+// A contribution only ever waits for earlier contributions of its own class, so each
+// queue is served in FIFO order, and urgent tasks never wait behind the backlog of far
+// ones.
+enum PushClass : int { kNear = 0, kNext = 1, kFar = 2, NCLS = 3 };
 
 // Cache policy of loads and stores that other workgroups of the same launch produce or
 // consume: device scope (sc1), so they bypass the non-coherent caches.
@@ -87,15 +91,15 @@ template <typename T>
 struct SweepArgs {
   int64_t m, n;
   int Mb, Nb, Nj, lo, hi, bits;
-  int qcap[2]; // band-update tasks of each class in the whole sweep
+  int qcap[NCLS]; // band-update tasks of each class in the whole sweep
   int nbxcd;  // band workers per XCD
   int gs;     // bands are dealt to the XCDs in groups of gs consecutive bands
   const T* Ua;
   const T* Ub;
   const T* s;
   const T* W;
-  T* Vacc[2];  // vertical feedback pushed by GEMM workers (subtracted from W), per class
-  T* Hacc[2];  // horizontal feedback pushed by GEMM workers, per class
+  T* Vacc[NCLS];  // vertical feedback pushed by GEMM workers (subtracted from W), per class
+  T* Hacc[NCLS];  // horizontal feedback pushed by GEMM workers, per class
   T* R;    // vertical residual, row-major m x n
   T* DT;   // Delta transposed, n x m
   int8_t* codes;
@@ -103,9 +107,9 @@ struct SweepArgs {
   int* info;
   int* ctl;                  // kCtlWords control words
   int* rdone;                // [Mb] micro-columns of each band whose R is stored
-  int* vcnt[2];              // [Mb * Nb] per class: contributions applied, per 64 x 64 tile
-  int* hcnt[2];              // [Mb * Nb] per class, horizontal
-  unsigned long long* qd[2]; // [qcap] per class: task descriptors (0 = not yet published)
+  int* vcnt[NCLS];              // [Mb * Nb] per class: contributions applied, per 64 x 64 tile
+  int* hcnt[NCLS];              // [Mb * Nb] per class, horizontal
+  unsigned long long* qd[NCLS]; // [qcap] per class: task descriptors (0 = not yet published)
   unsigned long long* stats; // band-update task accounting while profiling, else null
 };
 
@@ -121,13 +125,20 @@ struct SweepArgs {
 __host__ __device__ inline int nfar(int T) {
   return T >= GOUT + FAR_OFF ? (T - GOUT - FAR_OFF) / GOUT + 1 : 0;
 }
+// T is among the first kPanel targets of the far range of outer band nfar(T) - 1, whose
+// push to T is then of class kNext
+__host__ __device__ inline bool next_push(int T) {
+  return T >= GOUT + FAR_OFF && (T - GOUT - FAR_OFF) % GOUT < kPanel;
+}
 // contributions of one class that target T receives, and a contribution's rank in them
 __host__ __device__ inline int expected_class(int T, int cls) {
-  const int nf = nfar(T);
-  return cls == kFar ? nf : (T >= 2 ? T - 1 - GOUT * nf : 0);
+  const int nf = nfar(T), nx = next_push(T) ? 1 : 0;
+  if (cls == kNear) return T >= 2 ? T - 1 - GOUT * nf : 0;
+  return cls == kNext ? nx : nf - nx;
 }
-__host__ __device__ inline int push_seq(int T, int own, bool far) {
-  return far ? own / GOUT : own - GOUT * nfar(T);
+__host__ __device__ inline int push_seq(int T, int own, int cls) {
+  if (cls == kNear) return own - GOUT * nfar(T);
+  return cls == kNext ? 0 : own / GOUT;
 }
 __host__ __device__ inline void near_range(int own, int nt, int* t0, int* t1) {
   *t0 = own + 2;
@@ -148,16 +159,16 @@ __host__ __device__ inline int npanels(int t0, int t1) {
 }
 __host__ __device__ inline int block_task_count(int K, int L, int Mb, int Nb, int cls) {
   int t0, t1, c = 0;
-  if (cls == kNear) {
-    near_range(K, Mb, &t0, &t1);
-    c += npanels(t0, t1);
-    near_range(L, Nb, &t0, &t1);
-    c += npanels(t0, t1);
-  } else {
-    far_range(K, Mb, &t0, &t1);
-    c += npanels(t0, t1);
-    far_range(L, Nb, &t0, &t1);
-    c += npanels(t0, t1);
+  for (int dir = 0; dir < 2; ++dir) {
+    const int own = dir == 0 ? K : L, nt = dir == 0 ? Mb : Nb;
+    if (cls == kNear) {
+      near_range(own, nt, &t0, &t1);
+      c += npanels(t0, t1);
+    } else {
+      far_range(own, nt, &t0, &t1);
+      const int np = npanels(t0, t1);  // the first panel is the kNext task
+      c += cls == kNext ? (np > 0 ? 1 : 0) : (np > 0 ? np - 1 : 0);
+    }
   }
   return c;
 }
@@ -449,7 +460,7 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
   if (vblk != L) {
     const int64_t tile = (int64_t)K * a.Nb + L;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < NCLS; ++c) {
       const int evc = expected_class(K, c), ehc = expected_class(L, c);
       if (evc > 0 && !wait_ge(a.vcnt[c] + tile, evc, a.ctl, a.info)) return;
       if (ehc > 0 && !wait_ge(a.hcnt[c] + tile, ehc, a.ctl, a.info)) return;
@@ -460,7 +471,7 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
 #pragma unroll
   for (int e = 0; e < 4; ++e) hin[e] = T(0);
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < NCLS; ++c) {
     const rsrc_t rvf =
         make_rsrc(a.Vacc[c] + o0, expected_class(K, c) > 0 ? tile_bytes : 0);
     const rsrc_t rhf =
@@ -654,34 +665,57 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
   }
 }
 
-// Publishes the band-update tasks of completed block (K, L): near tasks into queue slots
-// base_near..., far tasks into base_far...; within a class vertical panels come first.
-// The lanes of one wave write the descriptors in parallel.
+// Publishes the band-update tasks of completed block (K, L): the tasks of class c go to
+// queue slots base[c]... (base[c] is lane c's value of `base`); within a class vertical
+// panels come first.  The lanes of one wave write the descriptors in parallel.
 template <typename T>
-__device__ inline void publish_block(const SweepArgs<T>& a, int K, int L, int base_near,
-                                     int base_far, int lane) {
-  int nv0, nv1, nh0, nh1, fv0, fv1, fh0, fh1;
-  near_range(K, a.Mb, &nv0, &nv1);
-  near_range(L, a.Nb, &nh0, &nh1);
-  far_range(K, a.Mb, &fv0, &fv1);
-  far_range(L, a.Nb, &fh0, &fh1);
-  const int nnv = npanels(nv0, nv1), nnh = npanels(nh0, nh1);
-  const int nfv = npanels(fv0, fv1), nfh = npanels(fh0, fh1);
-  const int nn = nnv + nnh, total = nn + nfv + nfh;
+__device__ inline void publish_block(const SweepArgs<T>& a, int K, int L, int base, int lane) {
+  // six groups (class, direction): first target, last target, panel count
+  int g0[6], g1[6], np[6];
+  for (int dir = 0; dir < 2; ++dir) {
+    const int own = dir == 0 ? K : L, nt = dir == 0 ? a.Mb : a.Nb;
+    int t0, t1;
+    near_range(own, nt, &t0, &t1);
+    g0[2 * kNear + dir] = t0;
+    g1[2 * kNear + dir] = t1;
+    np[2 * kNear + dir] = npanels(t0, t1);
+    far_range(own, nt, &t0, &t1);
+    const int nf = npanels(t0, t1);
+    g0[2 * kNext + dir] = t0;
+    g1[2 * kNext + dir] = t0 + kPanel - 1 < t1 ? t0 + kPanel - 1 : t1;
+    np[2 * kNext + dir] = nf > 0 ? 1 : 0;
+    g0[2 * kFar + dir] = t0 + kPanel;
+    g1[2 * kFar + dir] = t1;
+    np[2 * kFar + dir] = nf > 0 ? nf - 1 : 0;
+  }
+  int total = 0;
+#pragma unroll
+  for (int g = 0; g < 6; ++g) total += np[g];
+  int bs[NCLS];
+#pragma unroll
+  for (int c = 0; c < NCLS; ++c) bs[c] = __builtin_amdgcn_readlane(base, c);
   for (int i = lane; i < total; i += 64) {
-    const bool far = i >= nn;
-    const int k = far ? i - nn : i;  // index within the class
-    const int nvc = far ? nfv : nnv;
-    const int dir = k >= nvc ? 1 : 0;
-    const int pi = dir ? k - nvc : k;
-    const int t0 = far ? (dir ? fh0 : fv0) : (dir ? nh0 : nv0);
-    const int t1 = far ? (dir ? fh1 : fv1) : (dir ? nh1 : nv1);
-    const int p0 = t0 + kPanel * pi;
+    // group of item i and its index in the group, by constant-indexed selects
+    int g = 0, k = i, t0 = 0, t1 = 0, slot = 0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+      if (g == q && k >= np[q]) {
+        k -= np[q];
+        g = q + 1;
+      }
+#pragma unroll
+    for (int q = 0; q < 6; ++q)
+      if (g == q) {
+        t0 = g0[q];
+        t1 = g1[q];
+        slot = bs[q >> 1] + ((q & 1) ? np[q - 1] : 0);  // after the class's vertical panels
+      }
+    const int cls = g >> 1, dir = g & 1;
+    const int p0 = t0 + kPanel * k;
     const int p1 = p0 + kPanel - 1 < t1 ? p0 + kPanel - 1 : t1;
     const int own = dir == 0 ? K : L, other = dir == 0 ? L : K;
-    __hip_atomic_store((far ? a.qd[kFar] + base_far : a.qd[kNear] + base_near) + k,
-                       pack_task(far, dir, own, other, p0, p1), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.qd[cls] + slot + k, pack_task(cls != kNear, dir, own, other, p0, p1),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -756,7 +790,7 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
       // after the phase, so the atomics' latency overlaps the phase's work.
       const bool pub = w == nw - 1;
       int base = 0;
-      if (pub && closes && lane < 2) {
+      if (pub && closes && lane < NCLS) {
         const int cnt = block_task_count(K, cdone / GOUT, a.Mb, a.Nb, lane);
         if (cnt > 0) base = atomicAdd(a.ctl + kTail + kLine * lane, cnt);
       }
@@ -767,9 +801,7 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
       drain();
       __syncthreads();
       if (pub && cdone >= 0) {
-        if (closes)
-          publish_block(a, K, cdone / GOUT, __builtin_amdgcn_readlane(base, kNear),
-                        __builtin_amdgcn_readlane(base, kFar), lane);
+        if (closes) publish_block(a, K, cdone / GOUT, base, lane);
         if (lane == 0) st_dev(a.rdone + K, cdone + 1);
       }
     }
@@ -984,7 +1016,7 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm, int cls) {
         const int t1 = (d >> 15) & 0x7FFF, t0 = d & 0x7FFF;
         bool ok = true;
         for (int t = t0; t <= t1 && ok; ++t) {
-          const int seq = push_seq(t, own, far);
+          const int seq = push_seq(t, own, cls);
           int* cnt = dir == 0 ? a.vcnt[cls] + (int64_t)t * a.Nb + other
                               : a.hcnt[cls] + (int64_t)other * a.Nb + t;
           ok = wait_ge(cnt, seq, a.ctl, a.info);
@@ -1039,7 +1071,7 @@ __device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm, int cls) {
       for (int t = t0; t <= t1; ++t) {
         int* cnt = dir == 0 ? a.vcnt[cls] + (int64_t)t * a.Nb + other
                             : a.hcnt[cls] + (int64_t)other * a.Nb + t;
-        st_dev(cnt, push_seq(t, own, far) + 1);
+        st_dev(cnt, push_seq(t, own, cls) + 1);
       }
       if (a.stats) {
         atomicAdd(a.stats + 0, (unsigned long long)(wall_clock64() - t_begin));
@@ -1056,11 +1088,11 @@ struct SweepSmem {
   static constexpr size_t kBytes = kBand > kGemm ? kBand : kGemm;
 };
 
-// The persistent sweep.  Workgroups draw a ticket on their XCD when they start: ticket 0
-// of every XCD takes far band-update tasks and ticket 1 near ones (so both queues make
-// progress however many workgroups are resident), tickets 2 .. nbxcd + 1 own bands of
-// their XCD and take far tasks once no band is left, and of the rest one in four takes
-// near tasks and three far ones.
+// The persistent sweep.  Workgroups draw a ticket on their XCD when they start: tickets
+// 0, 1, 2 of every XCD take far, near and next band-update tasks (so every queue makes
+// progress however many workgroups are resident), tickets 3 .. nbxcd + 2 own bands of
+// their XCD and take far tasks once no band is left, and of the rest one in seven takes
+// near tasks, one in twenty next tasks and the others far ones.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_sweep(SweepArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[SweepSmem<T>::kBytes];
@@ -1068,8 +1100,12 @@ __global__ __launch_bounds__(kThreads) void k_sweep(SweepArgs<T> a) {
   if (threadIdx.x == 0) ticket = atomicAdd(a.ctl + kXTicket + kLine * xcd_id(), 1);
   __syncthreads();
   const int tk = ticket;
-  if (tk >= 2 && tk < 2 + a.nbxcd) band_worker<T>(a, *reinterpret_cast<BandSmem<T>*>(smem));
-  const int cls = (tk == 1 || (tk >= 2 + a.nbxcd && tk % 4 == 0)) ? kNear : kFar;
+  if (tk >= 3 && tk < 3 + a.nbxcd) band_worker<T>(a, *reinterpret_cast<BandSmem<T>*>(smem));
+  const int r = tk - 3 - a.nbxcd;
+  const int cls = tk < 3 ? (tk == 0 ? kFar : tk == 1 ? kNear : kNext)
+                  : r < 0 ? kFar
+                  : r % 7 == 0 ? kNear
+                  : r % 20 == 5 ? kNext : kFar;
   gemm_worker<T>(a, *reinterpret_cast<GemmSmem<T>*>(smem), cls);
 }
 
@@ -1090,24 +1126,26 @@ __global__ __launch_bounds__(256) void k_check_scales(int64_t m, const T* __rest
 }
 
 struct SyncLayout {
-  int64_t ctl, rdone, cnt, qd[2], words;  // offsets in ints; qd 8-byte aligned
-  int qcap[2];
+  int64_t ctl, rdone, cnt, qd[NCLS], words;  // offsets in ints; qd 8-byte aligned
+  int qcap[NCLS];
 };
 SyncLayout sync_layout(int64_t m, int64_t n) {
   const int Mb = (int)cdiv(m, BB), Nb = (int)cdiv(n, BB);
-  int64_t cap[2] = {0, 0};
+  int64_t cap[NCLS] = {0, 0, 0};
   for (int K = 0; K < Mb; ++K)
     for (int L = 0; L < Nb; ++L)
-      for (int c = 0; c < 2; ++c) cap[c] += block_task_count(K, L, Mb, Nb, c);
+      for (int c = 0; c < NCLS; ++c) cap[c] += block_task_count(K, L, Mb, Nb, c);
   SyncLayout s;
   s.ctl = 0;
   s.rdone = kCtlWords;
-  s.cnt = s.rdone + Mb;  // vcnt[near], vcnt[far], hcnt[near], hcnt[far]
-  s.qd[0] = (s.cnt + 4 * (int64_t)Mb * Nb + 1) / 2 * 2;
-  s.qd[1] = s.qd[0] + 2 * cap[0];
-  s.words = s.qd[1] + 2 * cap[1];
-  s.qcap[0] = (int)cap[0];
-  s.qcap[1] = (int)cap[1];
+  s.cnt = s.rdone + Mb;  // vcnt of each class, then hcnt of each class
+  int64_t q = (s.cnt + 2 * NCLS * (int64_t)Mb * Nb + 1) / 2 * 2;
+  for (int c = 0; c < NCLS; ++c) {
+    s.qd[c] = q;
+    q += 2 * cap[c];
+    s.qcap[c] = (int)cap[c];
+  }
+  s.words = q;
   return s;
 }
 
@@ -1137,19 +1175,19 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   a.Ub = Ub;
   a.s = scales;
   a.W = W;
-  a.Vacc[kNear] = take();
-  a.Vacc[kFar] = take();
-  a.Hacc[kNear] = take();
-  a.Hacc[kFar] = take();
+  for (int c = 0; c < NCLS; ++c) {
+    a.Vacc[c] = take();
+    a.Hacc[c] = take();
+  }
   a.R = take();
   a.DT = take();
   const SyncLayout sl = sync_layout(m, n);
   int* sync = (int*)c;
   a.ctl = sync + sl.ctl;
   a.rdone = sync + sl.rdone;
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < NCLS; ++c) {
     a.vcnt[c] = sync + sl.cnt + (int64_t)c * a.Mb * a.Nb;
-    a.hcnt[c] = sync + sl.cnt + (int64_t)(2 + c) * a.Mb * a.Nb;
+    a.hcnt[c] = sync + sl.cnt + (int64_t)(NCLS + c) * a.Mb * a.Nb;
     a.qd[c] = (unsigned long long*)(sync + sl.qd[c]);
     a.qcap[c] = sl.qcap[c];
   }
@@ -1175,11 +1213,11 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   if (nbw > grid / 2) nbw = grid / 2;
   if (nbw < 1) nbw = 1;
   // groups of up to eight consecutive bands per XCD, so that every XCD gets bands; one
-  // spare band worker per XCD, and two workgroups per XCD left for the two task queues
+  // spare band worker per XCD, and a workgroup per XCD left for each task queue
   a.gs = (a.Mb + NXCD - 1) / NXCD < 8 ? (a.Mb + NXCD - 1) / NXCD : 8;
   a.nbxcd = (nbw + NXCD - 1) / NXCD + 1;
-  if (a.nbxcd > grid / NXCD - 2) a.nbxcd = grid / NXCD - 2;
-  if (a.nbxcd < 1 || grid < 3 * NXCD) return hipErrorInvalidConfiguration;
+  if (a.nbxcd > grid / NXCD - NCLS) a.nbxcd = grid / NXCD - NCLS;
+  if (a.nbxcd < 1) return hipErrorInvalidConfiguration;
 
   const bool pr = prof_on();
   const double es = (double)sizeof(T);
@@ -1225,7 +1263,8 @@ hipError_t band_stats_collect(double* cu_ms, double* flops, int64_t* tasks) {
 size_t sweep_workspace(int64_t m, int64_t n, int dtype) {
   const size_t es = dtype == 0 ? sizeof(float) : sizeof(double);
   const SyncLayout sl = sync_layout(m, n);
-  return 6 * align_up((size_t)m * n * es) + align_up((size_t)sl.words * sizeof(int));
+  return (2 * NCLS + 2) * align_up((size_t)m * n * es) +
+         align_up((size_t)sl.words * sizeof(int));
 }
 
 hipError_t sweep_enqueue(int64_t m, int64_t n, int bits, int dtype, const void* W,
