@@ -254,12 +254,13 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
   c += align_up((size_t)n * n * es);
   void* scratch = c;
   void* scratch_b = c + g2d::factor_workspace(m);
-  // A's factor on the caller's stream, B's on the library's second stream; the sweep
-  // waits for both.
+  // The factors: one persistent Cholesky launch for both on the caller's stream, B's
+  // reversal, inverse and finalisation on the library's second stream; the sweep waits
+  // for both streams.
   std::lock_guard<std::recursive_mutex> lock(g2d::lib_mutex());
   hipStream_t s1 = nullptr;
   hipEvent_t* ev = nullptr;
-  hipError_t e = g2d::aux_resources(2, &s1, &ev);
+  hipError_t e = g2d::aux_resources(4, &s1, &ev);
   if (e == hipSuccess) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) e = hipStreamWaitEvent(s1, ev[0], 0);
   if (e == hipSuccess)

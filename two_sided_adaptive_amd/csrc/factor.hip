@@ -217,40 +217,114 @@ __device__ inline void chol_inv_block(Mfma<double>::acc_t (&acc)[4], BlockSmem& 
   }
 }
 
-// One step s of the blocked right-looking Cholesky of the reversed matrix, in one launch.
-//  * Workgroups 0 .. nblk-s-1 ("critical"): workgroup c handles row tile i = s + c of block
-//    column s.  Each subtracts the previous panel's contribution from the diagonal tile
-//    (s, s) and factors it (every critical workgroup does this identically, so none waits
-//    for another); workgroup 0 writes L_ss and X_ss = L_ss^-1, the others update their tile
-//    (i, s) with the previous panel and solve L_is = A_is X_ss^T.
-//  * The remaining workgroups ("bulk") apply the previous panel to the trailing tiles
-//    (i, j), s < j <= i: A_ij -= L_i,s-1 L_j,s-1^T.
-// So the panel chain and the bulk trailing update of the previous step share a launch.
-__global__ __launch_bounds__(256, 2) void k_chol_step(int64_t p, int s, double* __restrict__ Ar,
-                                                      double* __restrict__ X, int* info,
-                                                      int side_code) {
-  typedef Mfma<double>::acc_t acc_t;
-  __shared__ union {
-    BlockSmem b;
-    TileSmem<double> t;
-  } sh;
-  const int nblk = (int)((p + NB - 1) / NB);
-  const int crit = nblk - s;
-  if ((int)blockIdx.x >= crit) {
-    const int rest = nblk - s - 1, idx = (int)blockIdx.x - crit;
-    const int bi = idx / rest, bj = idx % rest;
-    if (bj > bi) return;
-    const int i = s + 1 + bi, j = s + 1 + bj;
-    const int64_t ri = (int64_t)i * NB, cj = (int64_t)j * NB, ck = (int64_t)(s - 1) * NB;
-    const int M = (p - ri) < NB ? (int)(p - ri) : NB;
-    const int N = (p - cj) < NB ? (int)(p - cj) : NB;
+// Loads and stores of the Cholesky steps.  Inside one launch per step plain cached
+// accesses suffice (the launch boundary makes the previous step's results visible); the
+// persistent kernel below passes DEV = true: data that other workgroups of the same launch
+// write is then read and written at device scope, past the per-XCD L2s, which are not
+// coherent with each other.
+constexpr int kDevAux = 16;  // buffer cache policy: device-coherent
+template <bool DEV>
+__device__ inline double ld(rsrc_t r, uint32_t elem) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, 0, DEV ? kDevAux : 0);
+  return __hiloint2double((int)v[1], (int)v[0]);
+}
+template <bool DEV>
+__device__ inline void st(double* p, double v) {
+  if (DEV)
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                       (unsigned long long)__double_as_longlong(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+// The trailing update of one tile by one panel: A_ij -= L_ik L_jk^T (all 64 x 64 tiles of
+// the reversed matrix, k = panel block column).
+template <bool DEV>
+__device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar,
+                                 TileSmem<double>& sm) {
+  const int64_t ri = (int64_t)i * NB, cj = (int64_t)j * NB, ck = (int64_t)k * NB;
+  const int M = (p - ri) < NB ? (int)(p - ri) : NB;
+  const int N = (p - cj) < NB ? (int)(p - cj) : NB;
+  if (!DEV) {
     tile_gemm<double, false, true>(Ar + ri * p + ck, p, Ar + cj * p + ck, p, Ar + ri * p + cj, p,
-                                   M, N, 0, NB, -1.0, 1.0, sh.t);
+                                   M, N, 0, NB, -1.0, 1.0, sm);
     return;
   }
-  BlockSmem& sm = sh.b;
+  // the same product with device-scope accesses: both operands i-major 64 x 64, staged
+  // k-major through LDS in two chunks
+  typedef Mfma<double>::acc_t acc_t;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wr = w >> 1, wc = w & 1, kr = lane >> 4, cl = lane & 15;
+  const rsrc_t ra = make_rsrc(Ar + ri * p + ck, ((int64_t)(M - 1) * p + NB) * 8);
+  const rsrc_t rb = make_rsrc(Ar + cj * p + ck, ((int64_t)(N - 1) * p + NB) * 8);
+  const rsrc_t rc = make_rsrc(Ar + ri * p + cj, ((int64_t)(M - 1) * p + N) * 8);
+  acc_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = acc_t{0, 0, 0, 0};
+  const int i4 = tid >> 2, k8 = (tid & 3) * 8;
+  double va[2][8], vb[2][8], old[2][2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      va[h][u] = ld<true>(ra, (uint32_t)((int64_t)i4 * p + 32 * h + k8 + u));
+      vb[h][u] = ld<true>(rb, (uint32_t)((int64_t)i4 * p + 32 * h + k8 + u));
+    }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 32 * wr + 16 * a + Mfma<double>::row(lane, e), jj = 32 * wc + 16 * b + cl;
+        old[a][b][e] = ld<true>(rc, (uint32_t)((int64_t)ii * p + jj));
+      }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sm.a[k8 + u][i4] = va[h][u];
+      sm.b[k8 + u][i4] = vb[h][u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kKc; kk += 4) {
+      double av[2], bv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        av[t] = sm.a[kk + kr][32 * wr + 16 * t + cl];
+        bv[t] = sm.b[kk + kr][32 * wc + 16 * t + cl];
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = Mfma<double>::run(av[a], bv[b], acc[a][b]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 32 * wr + 16 * a + Mfma<double>::row(lane, e), jj = 32 * wc + 16 * b + cl;
+        if (ii < M && jj < N) st<true>(&Ar[(ri + ii) * p + cj + jj], old[a][b][e] - acc[a][b][e]);
+      }
+}
+
+// The panel step of row tile i of block column s: subtract the previous panel's
+// contribution from the diagonal tile (s, s) and tile (i, s), factor (s, s) (every row
+// tile does this identically, so none waits for another), then the diagonal row tile
+// writes L_ss and X_ss = L_ss^-1 and the others solve L_is = A_is X_ss^T.
+template <bool DEV>
+__device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X, int* info,
+                                 int side_code, BlockSmem& sm) {
+  typedef Mfma<double>::acc_t acc_t;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, cl = lane & 15, kq = lane >> 4;
-  const int i = s + (int)blockIdx.x;
   const int64_t r0 = (int64_t)s * NB, ri = (int64_t)i * NB;
   const int nv = (p - r0) < NB ? (int)(p - r0) : NB;  // rows/columns of block s
   const int mi = (p - ri) < NB ? (int)(p - ri) : NB;  // rows of tile i
@@ -267,8 +341,8 @@ __global__ __launch_bounds__(256, 2) void k_chol_step(int64_t p, int s, double* 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * w + Mfma<double>::row(lane, e), k = 16 * t + cl;
-        v[t][e] = buf_load<double>(rd, (uint32_t)(r * p + k));
-        u[t][e] = diag ? 0.0 : buf_load<double>(rp, (uint32_t)(r * p + k));
+        v[t][e] = ld<DEV>(rd, (uint32_t)(r * p + k));
+        u[t][e] = diag ? 0.0 : ld<DEV>(rp, (uint32_t)(r * p + k));
       }
     if (s > 0) {
       const int64_t cp = (int64_t)(s - 1) * NB;  // block column s-1 is full width
@@ -278,8 +352,8 @@ __global__ __launch_bounds__(256, 2) void k_chol_step(int64_t p, int s, double* 
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
         const int idx = tid + 256 * it, r = idx >> 6, k = idx & 63;
-        a1[it] = buf_load<double>(rs, (uint32_t)(r * p + k));
-        a2[it] = diag ? 0.0 : buf_load<double>(rq, (uint32_t)(r * p + k));
+        a1[it] = ld<DEV>(rs, (uint32_t)(r * p + k));
+        a2[it] = diag ? 0.0 : ld<DEV>(rq, (uint32_t)(r * p + k));
       }
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
@@ -325,8 +399,10 @@ __global__ __launch_bounds__(256, 2) void k_chol_step(int64_t p, int s, double* 
     for (int idx = tid; idx < NB * NB; idx += 256) {
       const int r = idx >> 6, k = idx & 63;
       if (r < nv && k < nv) {
-        if (k <= r) Ar[(r0 + r) * p + r0 + k] = sm.lf[r][k];
-        X[(r0 + r) * p + r0 + k] = sm.xf[r][k];
+        // (L_ss itself is read by nothing later; in the persistent kernel other panel
+        // steps of this block column may still be reading the tile, so it stays)
+        if (!DEV && k <= r) st<DEV>(&Ar[(r0 + r) * p + r0 + k], sm.lf[r][k]);
+        st<DEV>(&X[(r0 + r) * p + r0 + k], sm.xf[r][k]);
       }
     }
     return;
@@ -346,8 +422,212 @@ __global__ __launch_bounds__(256, 2) void k_chol_step(int64_t p, int s, double* 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * w + Mfma<double>::row(lane, e), k = 16 * t + cl;
-      if (r < mi && k < nv) Ar[(ri + r) * p + r0 + k] = o[e];
+      if (r < mi && k < nv) st<DEV>(&Ar[(ri + r) * p + r0 + k], o[e]);
     }
+  }
+}
+
+// One step s of the blocked right-looking Cholesky of the reversed matrix, in one launch.
+//  * Workgroups 0 .. nblk-s-1 ("critical"): workgroup c runs the panel step of row tile
+//    i = s + c of block column s (chol_crit).
+//  * The remaining workgroups ("bulk") apply the previous panel to the trailing tiles
+//    (i, j), s < j <= i: A_ij -= L_i,s-1 L_j,s-1^T.
+// So the panel chain and the bulk trailing update of the previous step share a launch.
+__global__ __launch_bounds__(256, 2) void k_chol_step(int64_t p, int s, double* __restrict__ Ar,
+                                                      double* __restrict__ X, int* info,
+                                                      int side_code) {
+  __shared__ union {
+    BlockSmem b;
+    TileSmem<double> t;
+  } sh;
+  const int nblk = (int)((p + NB - 1) / NB);
+  const int crit = nblk - s;
+  if ((int)blockIdx.x >= crit) {
+    const int rest = nblk - s - 1, idx = (int)blockIdx.x - crit;
+    const int bi = idx / rest, bj = idx % rest;
+    if (bj > bi) return;
+    chol_bulk<false>(p, s - 1, s + 1 + bi, s + 1 + bj, Ar, sh.t);
+    return;
+  }
+  chol_crit<false>(p, s, s + (int)blockIdx.x, Ar, X, info, side_code, sh.b);
+}
+
+// ---------------------------------------------------------------------------
+// The whole blocked Cholesky of one or two matrices as one persistent kernel
+// ---------------------------------------------------------------------------
+// The per-step launches above serialise the panel chain with a launch boundary per step.
+// Here every workgroup takes tasks from one queue in a fixed order; a task waits (bounded)
+// until the tasks it depends on are done, so the chain of panel steps runs back to back
+// while the trailing updates fill the other CUs.  Tasks of matrix q, step s:
+//   bulk(s): tile (i, j), s + 1 <= j <= i, takes panel s - 1 (needs L_i,s-1 and L_j,s-1
+//            and the tile's panels 0 .. s - 2; afterwards the tile has s panels);
+//   crit(s): the panel step of row tile i >= s (needs L_s,s-1 and L_i,s-1 and the tiles
+//            (s, s), (i, s) with panels 0 .. s - 2; afterwards (i, s) holds L_is, final).
+// Group (q, s) lists bulk(s) of column s + 1 first, then crit(s), then the rest of bulk(s)
+// column by column; groups go by step, the matrices alternating.  Every task depends only
+// on earlier tasks, so the queue always drains.
+constexpr int kMaxChol = 2;
+struct CholMat {
+  int64_t p;
+  int nblk, side_code;
+  double* Ar;
+  double* X;
+  int* tile_cnt;   // [nblk * nblk] panels applied to each tile by bulk tasks (kFinal: L)
+};
+struct CholArgs {
+  CholMat mat[kMaxChol];
+  int nmat, maxn;
+  int64_t total;
+  int* ctl;  // [0] next task, [32] abort
+  int* info;
+};
+constexpr int kCholSpin = 1 << 20;
+constexpr int kFinal = 1 << 24;  // tile counter of a panel tile whose L is written
+
+// Tasks in group (q, s): n - s - 1 + n - s + (n - s - 2)(n - s - 1) / 2 = u (u + 1) / 2 with
+// u = n - s for s >= 1, and n for s = 0 (panel steps only).  Tasks of one matrix before
+// step S: n + sum_{u = n-S+1}^{n-1} u (u + 1) / 2 = n + T(n - 1) - T(n - S), T(k) =
+// k (k + 1) (k + 2) / 6.
+__host__ __device__ inline int64_t chol_tet(int64_t k) { return k * (k + 1) * (k + 2) / 6; }
+__host__ __device__ inline int64_t chol_group_size(int n, int s) {
+  const int64_t u = n - s;
+  return s == 0 ? n : u * (u + 1) / 2;
+}
+__host__ __device__ inline int64_t chol_before(int n, int S) {
+  if (S <= 0) return 0;
+  if (S > n) S = n;
+  return n + chol_tet(n - 1) - chol_tet(n - S);
+}
+
+// whole-wave bounded wait until *cnt >= v (false after an abort or a timeout)
+__device__ inline bool chol_wait(const int* cnt, int v, int* ctl, int* info) {
+  for (int it = 0;; ++it) {
+    const int x = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (x >= v) return true;
+    if ((it & 15) == 15) {
+      if (__hip_atomic_load(ctl + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+        return false;
+      if (it > kCholSpin) {
+        if ((threadIdx.x & 63) == 0 && atomicCAS(ctl + 32, 0, 1) == 0) record_info(info, 4, 0);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
+  __shared__ union {
+    BlockSmem b;
+    TileSmem<double> t;
+  } sh;
+  __shared__ int task[4];  // kind, matrix, row tile, step << 16 | column tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Every branch on the wave index is on a wave-uniform value, so that the compiler emits
+  // scalar branches: a barrier inside lane-divergent control flow would be reached a
+  // different number of times by different waves.
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (;;) {
+    if (w == 0) {
+      // wave 0 claims the next task (lane 0's atomic, broadcast) and decodes it
+      int tl = 0;
+      if (lane == 0) {
+        const bool ab =
+            __hip_atomic_load(a.ctl + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+        tl = ab ? -1 : atomicAdd(a.ctl, 1);
+      }
+      tl = __builtin_amdgcn_readfirstlane(tl);
+      const int64_t t = tl < 0 ? a.total : (int64_t)(unsigned)tl;
+      int kind = -1, q = 0, s = 0, i = 0, j = 0;
+      if (t < a.total) {
+        // the step: last s with (tasks of all matrices before step s) <= t
+        const int n0 = a.mat[0].nblk, n1 = a.nmat > 1 ? a.mat[1].nblk : 0;
+        int lo = 0, hi = a.maxn - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (chol_before(n0, mid) + chol_before(n1, mid) <= t) lo = mid;
+          else hi = mid - 1;
+        }
+        s = lo;
+        int64_t r = t - chol_before(n0, s) - chol_before(n1, s);
+        if (s < n0 && r < chol_group_size(n0, s)) {
+          q = 0;
+        } else {
+          if (s < n0) r -= chol_group_size(n0, s);
+          q = 1;
+        }
+        const int n = q == 0 ? n0 : n1;
+        int k = (int)r;
+        const int c1 = s >= 1 ? n - s - 1 : 0, c2 = n - s;
+        if (k < c1) {
+          kind = 0;
+          i = s + 1 + k;
+          j = s + 1;
+        } else if (k < c1 + c2) {
+          kind = 1;
+          i = s + (k - c1);
+        } else {
+          kind = 0;
+          k -= c1 + c2;
+          j = s + 2;
+          while (k >= n - j && j < n) {
+            k -= n - j;
+            ++j;
+          }
+          i = j + k;
+        }
+      }
+      if (lane == 0) {
+        task[0] = kind;
+        task[1] = q;
+        task[2] = i;
+        task[3] = (s << 16) | j;
+      }
+    }
+    __syncthreads();
+    const int kind = __builtin_amdgcn_readfirstlane(task[0]);
+    const int q = __builtin_amdgcn_readfirstlane(task[1]);
+    const int i = __builtin_amdgcn_readfirstlane(task[2]);
+    const int sj = __builtin_amdgcn_readfirstlane(task[3]);
+    const int s = sj >> 16, j = sj & 0xFFFF;
+    __syncthreads();  // task[] is rewritten by the next claim
+    if (kind < 0) return;
+    // select the matrix with branches (a runtime index into the kernel argument would
+    // copy it to scratch memory)
+    const CholMat m = q == 0 ? a.mat[0] : a.mat[1];
+    const int64_t p = m.p;
+    const int n = m.nblk;
+    // dependencies (wave 0 waits, the barrier releases the others)
+    if (w == 0) {
+      // the panel tiles this task reads are final (kFinal), and its own tiles carry panels
+      // 0 .. s - 2; every task polls only the few tiles it reads, so the waiters of one
+      // step spread over many words
+      const int* tc = m.tile_cnt;
+      const int r2 = kind == 0 ? j : s;  // the second panel row read
+      bool ok = true;
+      if (s >= 1) {
+        ok = chol_wait(tc + (int64_t)i * n + (s - 1), kFinal, a.ctl, a.info);
+        if (ok && r2 != i) ok = chol_wait(tc + (int64_t)r2 * n + (s - 1), kFinal, a.ctl, a.info);
+      }
+      if (ok && kind == 0) ok = chol_wait(tc + (int64_t)i * n + j, s - 1, a.ctl, a.info);
+      if (ok && kind == 1 && s >= 2) {
+        ok = chol_wait(tc + (int64_t)s * n + s, s - 1, a.ctl, a.info);
+        if (ok && i != s) ok = chol_wait(tc + (int64_t)i * n + s, s - 1, a.ctl, a.info);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __syncthreads();
+    if (kind == 0)
+      chol_bulk<true>(p, s - 1, i, j, m.Ar, sh.t);
+    else
+      chol_crit<true>(p, s, i, m.Ar, m.X, a.info, m.side_code, sh.b);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (w == 0 && lane == 0)
+      __hip_atomic_store(m.tile_cnt + (int64_t)i * n + (kind == 0 ? j : s), kind == 0 ? s : kFinal,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -406,7 +686,14 @@ struct FactorWs {
   double* X;
   double* Tb;
   int64_t ldt;
+  int* sync;  // persistent Cholesky: control words, then its counters (chol_sync_ints)
 };
+
+// ints of the persistent Cholesky's sync area: 64 control words, then the tile counters
+int64_t chol_sync_ints(int64_t p) {
+  const int64_t nb = cdiv(p, NB);
+  return 64 + nb * nb;
+}
 
 // Largest half-size used by the recursive doubling (the leading dimension of T).
 int64_t trtri_ldt(int64_t p) {
@@ -424,6 +711,8 @@ FactorWs carve(int64_t p, void* ws) {
   f.X = (double*)c;
   c += align_up((size_t)p * p * sizeof(double));
   f.Tb = (double*)c;
+  c += align_up((size_t)p * f.ldt * sizeof(double));
+  f.sync = (int*)c;
   return f;
 }
 
@@ -431,7 +720,8 @@ FactorWs carve(int64_t p, void* ws) {
 
 size_t factor_workspace(int64_t p) {
   const int64_t ldt = trtri_ldt(p);
-  return 2 * align_up((size_t)p * p * sizeof(double)) + align_up((size_t)p * ldt * sizeof(double));
+  return 2 * align_up((size_t)p * p * sizeof(double)) + align_up((size_t)p * ldt * sizeof(double)) +
+         align_up((size_t)chol_sync_ints(p) * sizeof(int));
 }
 
 // Dense GEMM flops of one launch (only evaluated while the measurement hook is on).
@@ -547,10 +837,72 @@ void stage(const FactorPlan& q, int idx) {
 
 }  // namespace
 
+// control words and counters start at zero (a fill kernel: the call may be captured)
+__global__ __launch_bounds__(256) void k_zero_ints(int* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0;
+}
+
+// The Cholesky of one or two matrices (plans qs[0..nmat)) as one persistent launch on s.
+hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int* info,
+                                   hipStream_t s) {
+  CholArgs a{};
+  a.nmat = nmat;
+  a.maxn = 0;
+  a.total = 0;
+  double fl = 0.0, by = 0.0;
+  const bool pr = prof_on();
+  for (int q = 0; q < nmat; ++q) {
+    const FactorPlan& pl = *qs[q];
+    const int nb = (int)cdiv(pl.p, NB);
+    a.mat[q].p = pl.p;
+    a.mat[q].nblk = nb;
+    a.mat[q].side_code = pl.side_code;
+    a.mat[q].Ar = pl.f.Ar;
+    a.mat[q].X = pl.f.X;
+    a.mat[q].tile_cnt = pl.f.sync + 64;
+    a.maxn = nb > a.maxn ? nb : a.maxn;
+    a.total += chol_before(nb, nb);
+    const int64_t words = chol_sync_ints(pl.p);
+    const int64_t zg = cdiv(words, 256) < 1024 ? cdiv(words, 256) : 1024;
+    k_zero_ints<<<(unsigned)zg, 256, 0, s>>>(pl.f.sync, words);
+    if (pr) {
+      const int64_t p = pl.p;
+      for (int st = 0; st < nb; ++st) {
+        const double nv = (double)((p - st * NB) < NB ? (p - st * NB) : NB);
+        const double rows = (double)(p - (int64_t)st * NB) - nv;
+        fl += 2.0 / 3.0 * nv * nv * nv + 2.0 * rows * nv * nv +
+              (st > 0 ? trailing_flops(p, st - 1) : 0.0);
+        const double trail = st > 0 ? (rows + nv) * (rows + nv + NB) / 2.0 : 0.0;
+        by += 8.0 * (3.0 * (rows + nv) * NB + 3.0 * trail);
+      }
+    }
+  }
+  a.ctl = qs[0]->f.sync;
+  a.info = info;
+  int dev = 0, ncu = 0, occ = 0;
+  hipError_t e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_chol_persistent, 256, 0)) !=
+      hipSuccess)
+    return e;
+  if (occ < 1) return hipErrorInvalidConfiguration;
+  prof_begin(KC_POTRF, s);
+  k_chol_persistent<<<ncu * occ, 256, 0, s>>>(a);
+  prof_end(KC_POTRF, s, fl, by);
+  return hipGetLastError();
+}
+
 hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws, int* info,
                           int side_code, hipStream_t s) {
   const FactorPlan q = plan(p, dtype, A, U, ws, info, side_code, s);
-  for (int i = 0; i < q.stages(); ++i) stage(q, i);
+  stage(q, 0);
+  const FactorPlan* qs[1] = {&q};
+  hipError_t e = chol_persistent_enqueue(qs, 1, info, s);
+  if (e != hipSuccess) return e;
+  for (int i = q.nblk + 1; i < q.stages(); ++i) stage(q, i);
   return hipGetLastError();
 }
 
@@ -559,12 +911,26 @@ hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, h
                                int dtype, int* info) {
   // launches alternate between the two chains so that both streams have work queued
   // from the start and the two factorisations overlap on the device
+  // reversal of each on its stream; both Cholesky factorisations in one persistent
+  // launch on sa; the inverses and the finalisation of each on its stream again
   const FactorPlan qa = plan(m, dtype, A, Ua, ws_a, info, 1, sa);
   const FactorPlan qb = plan(n, dtype, B, Ub, ws_b, info, 2, sb);
+  hipStream_t aux = nullptr;
+  hipEvent_t* ev = nullptr;
+  hipError_t e = aux_resources(4, &aux, &ev);
+  if (e != hipSuccess) return e;
+  stage(qa, 0);
+  stage(qb, 0);
+  if ((e = hipEventRecord(ev[3], sb)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sa, ev[3], 0)) != hipSuccess) return e;
+  const FactorPlan* qs[2] = {&qa, &qb};
+  if ((e = chol_persistent_enqueue(qs, 2, info, sa)) != hipSuccess) return e;
+  if ((e = hipEventRecord(ev[2], sa)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sb, ev[2], 0)) != hipSuccess) return e;
   const int na = qa.stages(), nb = qb.stages();
   for (int i = 0; i < (na > nb ? na : nb); ++i) {
-    if (i < na) stage(qa, i);
-    if (i < nb) stage(qb, i);
+    if (i > qa.nblk && i < na) stage(qa, i);
+    if (i > qb.nblk && i < nb) stage(qb, i);
   }
   return hipGetLastError();
 }
