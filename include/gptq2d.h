@@ -32,9 +32,10 @@
  *     runtime call fails.  Numerical failures are reported through `info`, a
  *     DEVICE int[2] that the call first clears (may be NULL): info[0] = 1 if A is
  *     not positive definite, 2 if B is not, 3 if a scale is <= 0 or not finite,
- *     4 if a dependency wait inside the persistent sweep kernel exceeded its bound
- *     (the kernel then stops early instead of hanging; this only happens when the
- *     device cannot keep the kernel's workgroups resident); info[1] = 1-based index
+ *     4 if a dependency wait inside one of the persistent kernels (the sweep, or the
+ *     Cholesky of the factor stage) exceeded its bound (the kernel then stops early
+ *     instead of hanging; this only happens when the device cannot keep the kernel's
+ *     workgroups resident); info[1] = 1-based index
  *     of the failing pivot or row.  When info[0] != 0 the outputs are undefined.
  *   - workspace: DEVICE scratch of at least the size returned by the matching
  *     *_workspace_bytes function, 256-byte aligned.  Passing NULL and 0 makes the

@@ -88,7 +88,7 @@ def _raise_rc(rc: int, fn: str) -> None:
 
 _INFO_MSG = {1: "A is not positive definite (pivot {})", 2: "B is not positive definite (pivot {})",
              3: "scale of row {} is not positive and finite",
-             4: "the sweep's internal dependency wait timed out (outputs undefined)"}
+             4: "a dependency wait inside a persistent kernel timed out (outputs undefined)"}
 
 
 def _check_info(info: torch.Tensor) -> None:
