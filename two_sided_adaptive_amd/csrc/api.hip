@@ -260,7 +260,7 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
   std::lock_guard<std::recursive_mutex> lock(g2d::lib_mutex());
   hipStream_t s1 = nullptr;
   hipEvent_t* ev = nullptr;
-  hipError_t e = g2d::aux_resources(4, &s1, &ev);
+  hipError_t e = g2d::aux_resources(g2d::kAuxEvents, &s1, &ev);
   if (e == hipSuccess) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) e = hipStreamWaitEvent(s1, ev[0], 0);
   if (e == hipSuccess)

@@ -477,7 +477,8 @@ struct CholMat {
 struct CholArgs {
   CholMat mat[kMaxChol];
   int nmat, maxn;
-  int64_t total;
+  int64_t total;  // tasks of the steps [s0, s1) of this launch
+  int64_t toff;   // tasks of all matrices before step s0
   int* ctl;  // [0] next task, [32] abort
   int* info;
 };
@@ -538,9 +539,9 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
         tl = ab ? -1 : atomicAdd(a.ctl, 1);
       }
       tl = __builtin_amdgcn_readfirstlane(tl);
-      const int64_t t = tl < 0 ? a.total : (int64_t)(unsigned)tl;
+      const int64_t t = (tl < 0 ? a.total : (int64_t)(unsigned)tl) + a.toff;
       int kind = -1, q = 0, s = 0, i = 0, j = 0;
-      if (t < a.total) {
+      if (t < a.total + a.toff) {
         // the step: last s with (tasks of all matrices before step s) <= t
         const int n0 = a.mat[0].nblk, n1 = a.nmat > 1 ? a.mat[1].nblk : 0;
         int lo = 0, hi = a.maxn - 1;
@@ -633,10 +634,11 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
 
 // Recursive doubling, step 1: T = L21 X11 for every pair of h-blocks (group z).
 // X11 is lower triangular, so column tile tj only needs k >= 64*tj.
-__global__ __launch_bounds__(256) void k_trtri_step1(int64_t p, int64_t h, const double* Ar,
-                                                     const double* X, double* Tb, int64_t ldt) {
+__global__ __launch_bounds__(256) void k_trtri_step1(int64_t p, int64_t h, int zoff,
+                                                     const double* Ar, const double* X, double* Tb,
+                                                     int64_t ldt) {
   __shared__ TileSmem<double> sm;
-  const int64_t g0 = (int64_t)blockIdx.z * 2 * h;
+  const int64_t g0 = (int64_t)(blockIdx.z + zoff) * 2 * h;
   const int64_t h1 = (p - g0) < h ? (p - g0) : h;
   const int64_t h2 = (p - g0 - h) < h ? (p - g0 - h) : h;
   const int64_t ti = blockIdx.y, tj = blockIdx.x;
@@ -650,10 +652,10 @@ __global__ __launch_bounds__(256) void k_trtri_step1(int64_t p, int64_t h, const
 }
 
 // Step 2: X21 = -X22 T.  X22 is lower triangular, so row tile ti only needs k < 64*(ti+1).
-__global__ __launch_bounds__(256) void k_trtri_step2(int64_t p, int64_t h, double* X,
+__global__ __launch_bounds__(256) void k_trtri_step2(int64_t p, int64_t h, int zoff, double* X,
                                                      const double* Tb, int64_t ldt) {
   __shared__ TileSmem<double> sm;
-  const int64_t g0 = (int64_t)blockIdx.z * 2 * h;
+  const int64_t g0 = (int64_t)(blockIdx.z + zoff) * 2 * h;
   const int64_t h1 = (p - g0) < h ? (p - g0) : h;
   const int64_t h2 = (p - g0 - h) < h ? (p - g0 - h) : h;
   const int64_t ti = blockIdx.y, tj = blockIdx.x;
@@ -686,7 +688,9 @@ struct FactorWs {
   double* X;
   double* Tb;
   int64_t ldt;
-  int* sync;  // persistent Cholesky: control words, then its counters (chol_sync_ints)
+  double* Tt;  // the top doubling level's T (rows ldt .. p-1, ldt wide): computed while the
+               // lower levels of the trailing block, which reuse Tb, are still to come
+  int* sync;   // persistent Cholesky: control words, then its counters (chol_sync_ints)
 };
 
 // ints of the persistent Cholesky's sync area: 64 control words, then the tile counters
@@ -712,6 +716,8 @@ FactorWs carve(int64_t p, void* ws) {
   c += align_up((size_t)p * p * sizeof(double));
   f.Tb = (double*)c;
   c += align_up((size_t)p * f.ldt * sizeof(double));
+  f.Tt = (double*)c;
+  c += align_up((size_t)(p > f.ldt ? p - f.ldt : 1) * f.ldt * sizeof(double));
   f.sync = (int*)c;
   return f;
 }
@@ -721,6 +727,7 @@ FactorWs carve(int64_t p, void* ws) {
 size_t factor_workspace(int64_t p) {
   const int64_t ldt = trtri_ldt(p);
   return 2 * align_up((size_t)p * p * sizeof(double)) + align_up((size_t)p * ldt * sizeof(double)) +
+         align_up((size_t)(p > ldt ? p - ldt : 1) * ldt * sizeof(double)) +
          align_up((size_t)chol_sync_ints(p) * sizeof(int));
 }
 
@@ -781,6 +788,26 @@ FactorPlan plan(int64_t p, int dtype, const void* A, void* U, void* ws, int* inf
   return q;
 }
 
+// One doubling level of the inverse over the groups [z0, z1) of width 2h: step 1
+// (T = L21 X11) if bit 0 of `steps` is set, step 2 (X21 = -X22 T) if bit 1 is.  The top
+// level (h == ldt) keeps T in its own buffer.
+void trtri_level(const FactorPlan& q, int64_t h, int z0, int z1, int steps) {
+  if (z1 <= z0) return;
+  const int64_t p = q.p;
+  FactorWs f = q.f;
+  // (T rows are addressed by their absolute index g0 + h + ..., >= ldt at the top level)
+  if (h == f.ldt) f.Tb = (double*)((char*)f.Tt - (size_t)f.ldt * f.ldt * sizeof(double));
+  const dim3 g((unsigned)cdiv(h, NB), (unsigned)cdiv(h, NB), (unsigned)(z1 - z0));
+  double f1 = 0.0, f2 = 0.0;
+  if (prof_on()) trtri_flops(p, h, &f1, &f2);
+  const double frac = (double)(z1 - z0) / (double)cdiv(p, 2 * h);  // (measurement only)
+  prof_begin(KC_TRTRI, q.s);
+  if (steps & 1) k_trtri_step1<<<g, 256, 0, q.s>>>(p, h, z0, f.Ar, f.X, f.Tb, f.ldt);
+  if (steps & 2) k_trtri_step2<<<g, 256, 0, q.s>>>(p, h, z0, f.X, f.Tb, f.ldt);
+  prof_end(KC_TRTRI, q.s, frac * (((steps & 1) ? f1 : 0.0) + ((steps & 2) ? f2 : 0.0)),
+           frac * 8.0 * 2.0 * (double)h * (double)p * (((steps & 1) ? 1 : 0) + ((steps & 2) ? 1 : 0)));
+}
+
 void stage(const FactorPlan& q, int idx) {
   const int64_t p = q.p;
   const bool pr = prof_on();
@@ -817,14 +844,7 @@ void stage(const FactorPlan& q, int idx) {
   }
   if (idx <= q.nblk + q.nlev) {
     const int64_t h = (int64_t)NB << (idx - q.nblk - 1);
-    const int64_t groups = cdiv(p, 2 * h);
-    const dim3 g((unsigned)cdiv(h, NB), (unsigned)cdiv(h, NB), (unsigned)groups);
-    double f1 = 0.0, f2 = 0.0;
-    if (pr) trtri_flops(p, h, &f1, &f2);
-    prof_begin(KC_TRTRI, s);
-    k_trtri_step1<<<g, 256, 0, s>>>(p, h, f.Ar, f.X, f.Tb, f.ldt);
-    k_trtri_step2<<<g, 256, 0, s>>>(p, h, f.X, f.Tb, f.ldt);
-    prof_end(KC_TRTRI, s, f1 + f2, 8.0 * 4.0 * (double)h * (double)p);
+    trtri_level(q, h, 0, (int)cdiv(p, 2 * h), 3);
     return;
   }
   prof_begin(KC_OTHER, s);
@@ -843,13 +863,16 @@ __global__ __launch_bounds__(256) void k_zero_ints(int* p, int64_t n) {
     p[i] = 0;
 }
 
-// The Cholesky of one or two matrices (plans qs[0..nmat)) as one persistent launch on s.
-hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int* info,
-                                   hipStream_t s) {
+// Steps [s0, s1) of the Cholesky of one or two matrices (plans qs[0..nmat)) as one
+// persistent launch on s, on at most `per_cu` workgroups per CU.  The first launch
+// (s0 == 0) clears the counters; a later one only the task counter and abort flag.
+hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int s0, int s1,
+                                   int per_cu, int* info, hipStream_t s) {
   CholArgs a{};
   a.nmat = nmat;
   a.maxn = 0;
   a.total = 0;
+  a.toff = 0;
   double fl = 0.0, by = 0.0;
   const bool pr = prof_on();
   for (int q = 0; q < nmat; ++q) {
@@ -862,13 +885,14 @@ hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int* i
     a.mat[q].X = pl.f.X;
     a.mat[q].tile_cnt = pl.f.sync + 64;
     a.maxn = nb > a.maxn ? nb : a.maxn;
-    a.total += chol_before(nb, nb);
-    const int64_t words = chol_sync_ints(pl.p);
+    a.total += chol_before(nb, s1) - chol_before(nb, s0);
+    a.toff += chol_before(nb, s0);
+    const int64_t words = s0 == 0 ? chol_sync_ints(pl.p) : (q == 0 ? 64 : 0);
     const int64_t zg = cdiv(words, 256) < 1024 ? cdiv(words, 256) : 1024;
-    k_zero_ints<<<(unsigned)zg, 256, 0, s>>>(pl.f.sync, words);
+    if (words > 0) k_zero_ints<<<(unsigned)zg, 256, 0, s>>>(pl.f.sync, words);
     if (pr) {
       const int64_t p = pl.p;
-      for (int st = 0; st < nb; ++st) {
+      for (int st = s0; st < (s1 < nb ? s1 : nb); ++st) {
         const double nv = (double)((p - st * NB) < NB ? (p - st * NB) : NB);
         const double rows = (double)(p - (int64_t)st * NB) - nv;
         fl += 2.0 / 3.0 * nv * nv * nv + 2.0 * rows * nv * nv +
@@ -889,6 +913,7 @@ hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int* i
       hipSuccess)
     return e;
   if (occ < 1) return hipErrorInvalidConfiguration;
+  if (occ > per_cu) occ = per_cu;
   prof_begin(KC_POTRF, s);
   k_chol_persistent<<<ncu * occ, 256, 0, s>>>(a);
   prof_end(KC_POTRF, s, fl, by);
@@ -900,7 +925,7 @@ hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws
   const FactorPlan q = plan(p, dtype, A, U, ws, info, side_code, s);
   stage(q, 0);
   const FactorPlan* qs[1] = {&q};
-  hipError_t e = chol_persistent_enqueue(qs, 1, info, s);
+  hipError_t e = chol_persistent_enqueue(qs, 1, 0, q.nblk, 2, info, s);
   if (e != hipSuccess) return e;
   for (int i = q.nblk + 1; i < q.stages(); ++i) stage(q, i);
   return hipGetLastError();
@@ -909,28 +934,64 @@ hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws
 hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, hipStream_t sa,
                                int64_t n, const void* B, void* Ub, void* ws_b, hipStream_t sb,
                                int dtype, int* info) {
-  // launches alternate between the two chains so that both streams have work queued
-  // from the start and the two factorisations overlap on the device
-  // reversal of each on its stream; both Cholesky factorisations in one persistent
-  // launch on sa; the inverses and the finalisation of each on its stream again
+  // Reversal of each on its stream; both Cholesky factorisations together in persistent
+  // launches on sa; the inverses and the finalisation of each on its stream again.  The
+  // Cholesky is split at step S = H / 64, H = the inverse's top-level half-size: once
+  // block columns < S are final, the inverse of the leading H x H block and the product
+  // T = L21 X11 of the top level need nothing else, so they run on sb while the rest of
+  // the Cholesky (a dependency chain that leaves most CUs idle) runs on sa with one
+  // workgroup per CU.
   const FactorPlan qa = plan(m, dtype, A, Ua, ws_a, info, 1, sa);
   const FactorPlan qb = plan(n, dtype, B, Ub, ws_b, info, 2, sb);
   hipStream_t aux = nullptr;
   hipEvent_t* ev = nullptr;
-  hipError_t e = aux_resources(4, &aux, &ev);
+  hipError_t e = aux_resources(kAuxEvents, &aux, &ev);
   if (e != hipSuccess) return e;
   stage(qa, 0);
   stage(qb, 0);
   if ((e = hipEventRecord(ev[3], sb)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(sa, ev[3], 0)) != hipSuccess) return e;
   const FactorPlan* qs[2] = {&qa, &qb};
-  if ((e = chol_persistent_enqueue(qs, 2, info, sa)) != hipSuccess) return e;
+  const FactorPlan* pl[2] = {&qa, &qb};
+  const int maxn = qa.nblk > qb.nblk ? qa.nblk : qb.nblk;
+  // split step: the smallest H / 64 of the matrices that have an inverse to compute
+  int S = maxn;
+  for (int k = 0; k < 2; ++k)
+    if (pl[k]->nlev > 0 && (int)(pl[k]->f.ldt / NB) < S) S = (int)(pl[k]->f.ldt / NB);
+  bool early[2];
+  for (int k = 0; k < 2; ++k) early[k] = pl[k]->nlev > 0 && pl[k]->f.ldt / NB <= S && S < maxn;
+  if ((e = chol_persistent_enqueue(qs, 2, 0, S, 2, info, sa)) != hipSuccess) return e;
   if ((e = hipEventRecord(ev[2], sa)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(sb, ev[2], 0)) != hipSuccess) return e;
-  const int na = qa.stages(), nb = qb.stages();
-  for (int i = 0; i < (na > nb ? na : nb); ++i) {
-    if (i > qa.nblk && i < na) stage(qa, i);
-    if (i > qb.nblk && i < nb) stage(qb, i);
+  // sb: the leading blocks' inverse levels and the top level's step 1 of each matrix
+  for (int k = 0; k < 2; ++k) {
+    if (!early[k]) continue;
+    FactorPlan q = *pl[k];
+    q.s = sb;
+    const int64_t H = q.f.ldt;
+    for (int64_t h = NB; h < H; h *= 2) trtri_level(q, h, 0, (int)(H / (2 * h)), 3);
+    trtri_level(q, H, 0, 1, 1);
+  }
+  if ((e = hipEventRecord(ev[4], sb)) != hipSuccess) return e;
+  if (S < maxn) {
+    if ((e = chol_persistent_enqueue(qs, 2, S, maxn, 1, info, sa)) != hipSuccess) return e;
+  }
+  if ((e = hipEventRecord(ev[5], sa)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sa, ev[4], 0)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sb, ev[5], 0)) != hipSuccess) return e;
+  // the rest of each inverse and the finalisation, A on sa and B on sb
+  for (int k = 0; k < 2; ++k) {
+    FactorPlan q = *pl[k];
+    q.s = k == 0 ? sa : sb;
+    if (early[k]) {
+      const int64_t H = q.f.ldt;
+      for (int64_t h = NB; h < H; h *= 2)
+        trtri_level(q, h, (int)(H / (2 * h)), (int)cdiv(q.p, 2 * h), 3);
+      trtri_level(q, H, 0, 1, 2);
+    } else {
+      for (int i = q.nblk + 1; i <= q.nblk + q.nlev; ++i) stage(q, i);
+    }
+    stage(q, q.nblk + q.nlev + 1);
   }
   return hipGetLastError();
 }
