@@ -113,7 +113,7 @@ size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype);
 /*
  * Measurement hook (not part of the method): when enabled, every kernel launch of
  * the library is bracketed by a pair of HIP events on its stream and accounted to a
- * kernel class (0 sweep, 2 Cholesky step, 3 trtri, 4 other) together with the
+ * kernel class (0 sweep, 2 factor: the persistent Cholesky and inverse, 3 other) with the
  * algorithmic flops and HBM bytes of that launch.  Class 1 (band_gemm) is counted
  * inside the persistent sweep kernel: its milliseconds are the summed busy time of the
  * workgroups that ran band-update tasks (CU-milliseconds), its launches the tasks and
@@ -121,7 +121,7 @@ size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype);
  * records to the stream and three atomics per band-update task while on.
  * gptq2d_profile_read waits for the recorded events, writes per-class totals since
  * the previous read (milliseconds, launches, flops, bytes; host arrays, any pointer
- * may be NULL) for the first min(n_classes, 5) classes and resets the totals.
+ * may be NULL) for the first min(n_classes, 4) classes and resets the totals.
  * Returns 0, -1 if n_classes < 0, or GPTQ2D_ERR_HIP if an event query failed.
  */
 int gptq2d_profile_enable(int on);

@@ -320,7 +320,7 @@ int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* fl
 }
 
 const char* gptq2d_profile_class_name(int cls) {
-  static const char* names[g2d::KC_COUNT] = {"sweep", "band_gemm", "chol", "trtri", "other"};
+  static const char* names[g2d::KC_COUNT] = {"sweep", "band_gemm", "factor", "other"};
   return (cls >= 0 && cls < g2d::KC_COUNT) ? names[cls] : "unknown";
 }
 

@@ -8,9 +8,10 @@
 //
 // Route (float64 throughout; MFMA f64 for the cubic parts):
 //   J A J = L L^T (lower Cholesky of the index-reversed matrix, blocked, right-looking,
-//            one launch per 64-wide step)
-//   X = L^-1 (diagonal 64-blocks inverted with their factorisation, the rest by
-//            recursive doubling: X21 = -X22 L21 X11)
+//            64-wide steps)
+//   X = L^-1 by 64-row blocks: X_ii = L_ii^-1 with the diagonal block's factorisation,
+//            X_is = -X_ii sum_{s<=k<i} L_ik X_ks below it, as soon as L's row block i is
+//            final; both in one persistent launch
 //   U = J X J is the upper Cholesky factor of A^-1; U'[i][j] = U[i][j] / U[i][i].
 // Diagonal-block inverses double as the panel solve: L21 = A21 (L11^-1)^T is a GEMM.
 #include <math.h>
@@ -217,15 +218,18 @@ __device__ inline void chol_inv_block(Mfma<double>::acc_t (&acc)[4], BlockSmem& 
   }
 }
 
-// Loads and stores of the Cholesky steps.  Inside one launch per step plain cached
-// accesses suffice (the launch boundary makes the previous step's results visible); the
-// persistent kernel below passes DEV = true: data that other workgroups of the same launch
-// write is then read and written at device scope, past the per-XCD L2s, which are not
-// coherent with each other.
+// Loads and stores of the Cholesky tasks.  Tiles that other workgroups of the same launch
+// update are read and written at device scope (DEV = true), past the per-XCD L2s, which
+// are not coherent with each other.  Final panel tiles are also copied, once, to a tiled
+// buffer that nothing else writes during the launch (Lt); their many readers load them
+// through the caches (DEV = false): a line of Lt can only enter a cache after the tile is
+// final, so no cached copy is ever stale.
 constexpr int kDevAux = 16;  // buffer cache policy: device-coherent
+// elem: per-lane element offset; sbytes: a wave-uniform byte offset (a compile-time
+// constant at every use, so that unrolled loads share one address register)
 template <bool DEV>
-__device__ inline double ld(rsrc_t r, uint32_t elem) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, 0, DEV ? kDevAux : 0);
+__device__ inline double ld(rsrc_t r, uint32_t elem, uint32_t sbytes = 0) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, elem * 8u, sbytes, DEV ? kDevAux : 0);
   return __hiloint2double((int)v[1], (int)v[0]);
 }
 template <bool DEV>
@@ -238,26 +242,33 @@ __device__ inline void st(double* p, double v) {
     *p = v;
 }
 
-// The trailing update of one tile by one panel: A_ij -= L_ik L_jk^T (all 64 x 64 tiles of
-// the reversed matrix, k = panel block column).
-template <bool DEV>
-__device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar,
+// Lt holds the strictly lower tiles (i, k), k < i, of L, each 64 x 64 row-major and
+// contiguous; rows past the matrix are never written and never read (a tile's buffer
+// descriptor covers its rows only, so loads past them return zeros).
+__device__ inline const double* lt_tile(const double* Lt, int i, int k) {
+  return Lt + ((int64_t)i * (i - 1) / 2 + k) * (NB * NB);
+}
+// Xt holds the final tiles (i, s), s <= i, of X = L^-1 the same way (written once).
+__device__ inline const double* xt_tile(const double* Xt, int i, int s) {
+  return Xt + ((int64_t)i * (i + 1) / 2 + s) * (NB * NB);
+}
+__device__ inline int tile_rows(int64_t p, int i) {
+  return (p - (int64_t)i * NB) < NB ? (int)(p - (int64_t)i * NB) : NB;
+}
+
+// The trailing update of one tile by one panel: A_ij -= L_ik L_jk^T (64 x 64 tiles of the
+// reversed matrix, k = panel block column).
+__device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar, const double* Lt,
                                  TileSmem<double>& sm) {
-  const int64_t ri = (int64_t)i * NB, cj = (int64_t)j * NB, ck = (int64_t)k * NB;
-  const int M = (p - ri) < NB ? (int)(p - ri) : NB;
-  const int N = (p - cj) < NB ? (int)(p - cj) : NB;
-  if (!DEV) {
-    tile_gemm<double, false, true>(Ar + ri * p + ck, p, Ar + cj * p + ck, p, Ar + ri * p + cj, p,
-                                   M, N, 0, NB, -1.0, 1.0, sm);
-    return;
-  }
-  // the same product with device-scope accesses: both operands i-major 64 x 64, staged
-  // k-major through LDS in two chunks
+  const int64_t ri = (int64_t)i * NB, cj = (int64_t)j * NB;
+  const int M = tile_rows(p, i), N = tile_rows(p, j);
+  // both operands i-major 64 x 64 from Lt, staged k-major through LDS in two chunks; the
+  // tile itself at device scope
   typedef Mfma<double>::acc_t acc_t;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wr = w >> 1, wc = w & 1, kr = lane >> 4, cl = lane & 15;
-  const rsrc_t ra = make_rsrc(Ar + ri * p + ck, ((int64_t)(M - 1) * p + NB) * 8);
-  const rsrc_t rb = make_rsrc(Ar + cj * p + ck, ((int64_t)(N - 1) * p + NB) * 8);
+  const rsrc_t ra = make_rsrc(lt_tile(Lt, i, k), (int64_t)M * NB * 8);
+  const rsrc_t rb = make_rsrc(lt_tile(Lt, j, k), (int64_t)N * NB * 8);
   const rsrc_t rc = make_rsrc(Ar + ri * p + cj, ((int64_t)(M - 1) * p + N) * 8);
   acc_t acc[2][2];
 #pragma unroll
@@ -270,8 +281,8 @@ __device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar,
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      va[h][u] = ld<true>(ra, (uint32_t)((int64_t)i4 * p + 32 * h + k8 + u));
-      vb[h][u] = ld<true>(rb, (uint32_t)((int64_t)i4 * p + 32 * h + k8 + u));
+      va[h][u] = ld<false>(ra, (uint32_t)(i4 * NB + 32 * h + k8 + u));
+      vb[h][u] = ld<false>(rb, (uint32_t)(i4 * NB + 32 * h + k8 + u));
     }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -319,10 +330,13 @@ __device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar,
 // The panel step of row tile i of block column s: subtract the previous panel's
 // contribution from the diagonal tile (s, s) and tile (i, s), factor (s, s) (every row
 // tile does this identically, so none waits for another), then the diagonal row tile
-// writes L_ss and X_ss = L_ss^-1 and the others solve L_is = A_is X_ss^T.
-template <bool DEV>
-__device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X, int* info,
-                                 int side_code, BlockSmem& sm) {
+// writes X_ss = L_ss^-1 to X and Xt and the others solve L_is = A_is X_ss^T and write it
+// to Ar and Lt.
+// (L_ss itself is read by nothing later; other panel steps of this block column may still
+// be reading tile (s, s), so it stays.)
+__device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X, double* Lt,
+                                 double* Xt, int* info, int side_code, BlockSmem& sm) {
+  constexpr bool DEV = true;
   typedef Mfma<double>::acc_t acc_t;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, cl = lane & 15, kq = lane >> 4;
   const int64_t r0 = (int64_t)s * NB, ri = (int64_t)i * NB;
@@ -345,19 +359,18 @@ __device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X,
         u[t][e] = diag ? 0.0 : ld<DEV>(rp, (uint32_t)(r * p + k));
       }
     if (s > 0) {
-      const int64_t cp = (int64_t)(s - 1) * NB;  // block column s-1 is full width
-      const rsrc_t rs = make_rsrc(Ar + r0 * p + cp, ((int64_t)(nv - 1) * p + NB) * 8);
-      const rsrc_t rq = make_rsrc(Ar + ri * p + cp, ((int64_t)(mi - 1) * p + NB) * 8);
+      // L_s,s-1 and L_i,s-1 from Lt (rows past the matrix read as zeros)
+      const rsrc_t rs = make_rsrc(lt_tile(Lt, s, s - 1), (int64_t)nv * NB * 8);
+      const rsrc_t rq = make_rsrc(lt_tile(Lt, i, s - 1), (int64_t)mi * NB * 8);
       double a1[16], a2[16];
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
-        const int idx = tid + 256 * it, r = idx >> 6, k = idx & 63;
-        a1[it] = ld<DEV>(rs, (uint32_t)(r * p + k));
-        a2[it] = diag ? 0.0 : ld<DEV>(rq, (uint32_t)(r * p + k));
+        a1[it] = ld<false>(rs, (uint32_t)tid, 2048u * it);
+        a2[it] = diag ? 0.0 : ld<false>(rq, (uint32_t)tid, 2048u * it);
       }
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
-        const int idx = tid + 256 * it, r = idx >> 6, k = idx & 63;
+        const int r = (tid >> 6) + 4 * it, k = tid & 63;  // element tid + 256 it
         sm.lf[r][k] = a1[it];
         sm.xf[r][k] = a2[it];
       }
@@ -366,7 +379,11 @@ __device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X,
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + Mfma<double>::row(lane, e), k = 16 * t + cl;
+        int r = 16 * w + Mfma<double>::row(lane, e);
+        const int k = 16 * t + cl;
+        // (an opaque copy of the row: otherwise the compiler keeps all 16 padding values of
+        // the lane live across the task loop)
+        __asm__ volatile("" : "+v"(r));
         acc[t][e] = (r < nv && k < nv) ? (k <= r ? v[t][e] : 0.0) : (r == k ? 1.0 : 0.0);
         pt[t][e] = u[t][e];
       }
@@ -398,16 +415,15 @@ __device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X,
     }
     for (int idx = tid; idx < NB * NB; idx += 256) {
       const int r = idx >> 6, k = idx & 63;
-      if (r < nv && k < nv) {
-        // (L_ss itself is read by nothing later; in the persistent kernel other panel
-        // steps of this block column may still be reading the tile, so it stays)
-        if (!DEV && k <= r) st<DEV>(&Ar[(r0 + r) * p + r0 + k], sm.lf[r][k]);
-        st<DEV>(&X[(r0 + r) * p + r0 + k], sm.xf[r][k]);
-      }
+      if (r < nv && k < nv) st<DEV>(&X[(r0 + r) * p + r0 + k], sm.xf[r][k]);
+      // the whole tile, padding included (identity past the matrix), for the row inverse
+      st<DEV>(const_cast<double*>(xt_tile(Xt, s, s)) + idx, sm.xf[r][k]);
     }
     return;
   }
-  // L_is = A_is X_ss^T: A_is goes through lf (free after the factorisation)
+  // L_is = A_is X_ss^T: A_is goes through lf (free after the factorisation); block column
+  // s is full width (i > s)
+  double* lt = const_cast<double*>(lt_tile(Lt, i, s));
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -422,82 +438,191 @@ __device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * w + Mfma<double>::row(lane, e), k = 16 * t + cl;
-      if (r < mi && k < nv) st<DEV>(&Ar[(ri + r) * p + r0 + k], o[e]);
+      if (r < mi) {
+        st<DEV>(&Ar[(ri + r) * p + r0 + k], o[e]);
+        st<DEV>(&lt[r * NB + k], o[e]);
+      }
     }
   }
 }
 
-// One step s of the blocked right-looking Cholesky of the reversed matrix, in one launch.
-//  * Workgroups 0 .. nblk-s-1 ("critical"): workgroup c runs the panel step of row tile
-//    i = s + c of block column s (chol_crit).
-//  * The remaining workgroups ("bulk") apply the previous panel to the trailing tiles
-//    (i, j), s < j <= i: A_ij -= L_i,s-1 L_j,s-1^T.
-// So the panel chain and the bulk trailing update of the previous step share a launch.
-__global__ __launch_bounds__(256, 2) void k_chol_step(int64_t p, int s, double* __restrict__ Ar,
-                                                      double* __restrict__ X, int* info,
-                                                      int side_code) {
-  __shared__ union {
-    BlockSmem b;
-    TileSmem<double> t;
-  } sh;
-  const int nblk = (int)((p + NB - 1) / NB);
-  const int crit = nblk - s;
-  if ((int)blockIdx.x >= crit) {
-    const int rest = nblk - s - 1, idx = (int)blockIdx.x - crit;
-    const int bi = idx / rest, bj = idx % rest;
-    if (bj > bi) return;
-    chol_bulk<false>(p, s - 1, s + 1 + bi, s + 1 + bj, Ar, sh.t);
-    return;
+// One chunk of the row-block inverse.  For i > s, X_is = -X_ii Y_is with
+// Y_is = sum_{k=s}^{i-1} L_ik X_ks (from L X = I, block row i).  The sum is split into
+// chunks of at most kInvDepth tiles of k, added oldest first: this task adds the tiles
+// k in [klo, khi) to the partial sum kept in X (the first chunk starts it), and the chunk
+// that ends at k = i - 1 (last) forms X_is and writes it to X and Xt.  L_ik and X_ks come
+// from Lt and Xt through the caches; the partial sums, which other workgroups rewrite, at
+// device scope.
+__device__ inline void chol_xchunk(int64_t p, int i, int s, int klo, int khi, bool first,
+                                   bool last, double* X, const double* Lt, double* Xt,
+                                   BlockSmem& sm) {
+  typedef Mfma<double>::acc_t acc_t;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wr = w >> 1, wc = w & 1, kr = lane >> 4, cl = lane & 15;
+  const int mi = tile_rows(p, i);
+  const int64_t ri = (int64_t)i * NB, cs = (int64_t)s * NB;  // block column s is full width
+  // staging: thread (column c, rows 16 h .. 16 h + 15) of both 64 x 64 operands, so that a
+  // wave loads whole rows and writes whole LDS rows
+  const int c = tid & 63, h16 = (tid >> 6) * 16;
+  double va[16], vb[16];
+  auto fetch = [&](int k) {
+    const rsrc_t ra = make_rsrc(lt_tile(Lt, i, k), (int64_t)mi * NB * 8);
+    const rsrc_t rb = make_rsrc(xt_tile(Xt, k, s), (int64_t)NB * NB * 8);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      va[u] = ld<false>(ra, (uint32_t)(h16 * NB + c), 512u * u);
+      vb[u] = ld<false>(rb, (uint32_t)(h16 * NB + c), 512u * u);
+    }
+  };
+  fetch(klo);
+  acc_t acc[2][2];
+  {
+    const rsrc_t rc = make_rsrc(X + ri * p + cs, ((int64_t)(mi - 1) * p + NB) * 8);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = 32 * wr + 16 * a + Mfma<double>::row(lane, e), jj = 32 * wc + 16 * b + cl;
+          acc[a][b][e] = first ? 0.0 : ld<true>(rc, (uint32_t)((int64_t)ii * p + jj));
+        }
   }
-  chol_crit<false>(p, s, s + (int)blockIdx.x, Ar, X, info, side_code, sh.b);
+  // acc += A B with A (row-major in lf) and B (row-major in xf), one 64-deep tile
+  auto mma = [&](double sign) {
+#pragma unroll
+    for (int kk = 0; kk < NB; kk += 4) {
+      double av[2], bv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        av[t] = sign * sm.lf[32 * wr + 16 * t + cl][kk + kr];
+        bv[t] = sm.xf[kk + kr][32 * wc + 16 * t + cl];
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = Mfma<double>::run(av[a], bv[b], acc[a][b]);
+    }
+  };
+  for (int k = klo; k < khi; ++k) {
+    __syncthreads();  // the previous tile's reads of lf / xf are done
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      sm.lf[h16 + u][c] = va[u];
+      sm.xf[h16 + u][c] = vb[u];
+    }
+    __syncthreads();
+    if (k + 1 < khi) fetch(k + 1);  // in flight during the products
+    mma(1.0);
+  }
+  if (last) {
+    // X_is = -X_ii Y_is: X_ii (padded with the identity past the matrix) in lf, Y in xf
+    const rsrc_t rd = make_rsrc(xt_tile(Xt, i, i), (int64_t)NB * NB * 8);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) va[u] = ld<false>(rd, (uint32_t)(h16 * NB + c), 512u * u);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) sm.lf[h16 + u][c] = va[u];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sm.xf[32 * wr + 16 * a + Mfma<double>::row(lane, e)][32 * wc + 16 * b + cl] = acc[a][b][e];
+          acc[a][b][e] = 0.0;
+        }
+    __syncthreads();
+    mma(-1.0);
+  }
+  double* xt = const_cast<double*>(xt_tile(Xt, i, s));
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = 32 * wr + 16 * a + Mfma<double>::row(lane, e), jj = 32 * wc + 16 * b + cl;
+        if (ii < mi) st<true>(&X[(ri + ii) * p + cs + jj], acc[a][b][e]);
+        if (last) st<true>(&xt[ii * NB + jj], acc[a][b][e]);
+      }
 }
 
 // ---------------------------------------------------------------------------
-// The whole blocked Cholesky of one or two matrices as one persistent kernel
+// The Cholesky and the inverse of one or two matrices as one persistent kernel
 // ---------------------------------------------------------------------------
-// The per-step launches above serialise the panel chain with a launch boundary per step.
-// Here every workgroup takes tasks from one queue in a fixed order; a task waits (bounded)
-// until the tasks it depends on are done, so the chain of panel steps runs back to back
-// while the trailing updates fill the other CUs.  Tasks of matrix q, step s:
-//   bulk(s): tile (i, j), s + 1 <= j <= i, takes panel s - 1 (needs L_i,s-1 and L_j,s-1
-//            and the tile's panels 0 .. s - 2; afterwards the tile has s panels);
-//   crit(s): the panel step of row tile i >= s (needs L_s,s-1 and L_i,s-1 and the tiles
-//            (s, s), (i, s) with panels 0 .. s - 2; afterwards (i, s) holds L_is, final).
-// Group (q, s) lists bulk(s) of column s + 1 first, then crit(s), then the rest of bulk(s)
-// column by column; groups go by step, the matrices alternating.  Every task depends only
-// on earlier tasks, so the queue always drains.
+// Every workgroup takes tasks from one queue in a fixed order; a task waits (bounded)
+// until the tasks it depends on are done, so the chain of panel steps runs back to back,
+// with no launch boundary per step, while the trailing updates and the inverse fill the
+// other CUs.  Tasks of matrix q, step g:
+//   bulk(g): tile (i, j), g + 1 <= j <= i, takes panel g - 1 (needs L_i,g-1 and L_j,g-1
+//            and the tile's panels 0 .. g - 2; afterwards the tile has g panels);
+//   crit(g): the panel step of row tile i >= g (needs L_g,g-1 and L_i,g-1 and the tiles
+//            (g, g), (i, g) with panels 0 .. g - 2; afterwards (i, g) holds L_ig, final;
+//            crit(g) of i = g also writes X_gg);
+//   xrow(g): chunk jj of X_is for i = g + kInvStride jj and every s with a non-empty
+//            chunk: k in [max(s, khi - kInvDepth), khi), khi = i - kInvDepth jj (needs
+//            L_i,khi-1 and X_khi-1,s final, and the tile's previous chunk; chunk 0 also
+//            X_ii).  A row's chunks thus sit in the steps just before its own, oldest
+//            chunk first.
+// Group (q, g) lists bulk(g) of column g + 1 first, then crit(g), then the rest of
+// bulk(g) column by column, then xrow(g) by jj and s; groups go by step, the matrices
+// alternating.  Every task depends only on earlier tasks, so the queue always drains.
+constexpr int kInvDepth = 8;   // tiles of k per chunk of the row inverse
+constexpr int kInvStride = 2;  // steps between the chunks of one row
 constexpr int kMaxChol = 2;
 struct CholMat {
   int64_t p;
   int nblk, side_code;
   double* Ar;
   double* X;
+  double* Lt;      // final off-diagonal tiles of L, tiled (written once)
+  double* Xt;      // final tiles of X, tiled (written once)
   int* tile_cnt;   // [nblk * nblk] panels applied to each tile by bulk tasks (kFinal: L)
+  int* xcnt;       // [nblk * nblk] chunks added to each tile of X (kFinal: X final)
+  const int* tab;  // [nblk + 1] tasks of this matrix before each step
 };
 struct CholArgs {
   CholMat mat[kMaxChol];
   int nmat, maxn;
-  int64_t total;  // tasks of the steps [s0, s1) of this launch
-  int64_t toff;   // tasks of all matrices before step s0
-  int* ctl;  // [0] next task, [32] abort
+  int64_t total;  // tasks of all matrices
+  int* ctl;       // [0] next task, [32] abort
   int* info;
 };
 constexpr int kCholSpin = 1 << 20;
-constexpr int kFinal = 1 << 24;  // tile counter of a panel tile whose L is written
+constexpr int kFinal = 1 << 24;  // tile counter of a final tile
 
-// Tasks in group (q, s): n - s - 1 + n - s + (n - s - 2)(n - s - 1) / 2 = u (u + 1) / 2 with
-// u = n - s for s >= 1, and n for s = 0 (panel steps only).  Tasks of one matrix before
-// step S: n + sum_{u = n-S+1}^{n-1} u (u + 1) / 2 = n + T(n - 1) - T(n - S), T(k) =
-// k (k + 1) (k + 2) / 6.
-__host__ __device__ inline int64_t chol_tet(int64_t k) { return k * (k + 1) * (k + 2) / 6; }
-__host__ __device__ inline int64_t chol_group_size(int n, int s) {
-  const int64_t u = n - s;
-  return s == 0 ? n : u * (u + 1) / 2;
+// Tasks in group (q, g) of the Cholesky: n - g - 1 + n - g + (n - g - 2)(n - g - 1) / 2
+// = u (u + 1) / 2 with u = n - g for g >= 1, and n for g = 0 (panel steps only).
+__host__ __device__ inline int64_t chol_group_size(int n, int g) {
+  const int64_t u = n - g;
+  return g == 0 ? n : u * (u + 1) / 2;
 }
-__host__ __device__ inline int64_t chol_before(int n, int S) {
-  if (S <= 0) return 0;
-  if (S > n) S = n;
-  return n + chol_tet(n - 1) - chol_tet(n - S);
+// xrow tasks of chunk jj in group g: the columns s < g - (kInvDepth - kInvStride) jj, while
+// the row g + kInvStride jj exists.
+__host__ __device__ inline int xrow_count(int n, int g, int jj) {
+  const int cnt = g - (kInvDepth - kInvStride) * jj;
+  return (g + kInvStride * jj < n && cnt > 0) ? cnt : 0;
+}
+__host__ __device__ inline int64_t group_size(int n, int g) {
+  int64_t c = chol_group_size(n, g);
+  for (int jj = 0; xrow_count(n, g, jj) > 0; ++jj) c += xrow_count(n, g, jj);
+  return c;
+}
+// chunks of the row inverse of tile (i, s), i > s
+__host__ __device__ inline int xrow_chunks(int i, int s) {
+  return (i - s + kInvDepth - 1) / kInvDepth;
+}
+
+// tab[g] = tasks of the matrix before step g (one thread; n + 1 entries)
+__global__ __launch_bounds__(64) void k_chol_table(int* tab, int n) {
+  if (threadIdx.x != 0) return;
+  int64_t t = 0;
+  for (int g = 0; g < n; ++g) {
+    tab[g] = (int)t;
+    t += group_size(n, g);
+  }
+  tab[n] = (int)t;
 }
 
 // whole-wave bounded wait until *cnt >= v (false after an abort or a timeout)
@@ -518,17 +643,29 @@ __device__ inline bool chol_wait(const int* cnt, int v, int* ctl, int* info) {
   }
 }
 
+__device__ inline int ld_uniform(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
+
 __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
   __shared__ union {
     BlockSmem b;
     TileSmem<double> t;
   } sh;
-  __shared__ int task[4];  // kind, matrix, row tile, step << 16 | column tile
+  __shared__ int task[4];  // kind, matrix, row tile, step (or column) << 16 | column (or jj)
   const int tid = threadIdx.x, lane = tid & 63;
   // Every branch on the wave index is on a wave-uniform value, so that the compiler emits
   // scalar branches: a barrier inside lane-divergent control flow would be reached a
   // different number of times by different waves.
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = a.mat[0].nblk, n1 = a.nmat > 1 ? a.mat[1].nblk : 0;
+  // wave 0's decode state: the step g of the last task and the task range [lo, hi) of
+  // step g (both matrices), with the size of matrix 0's group in it.  A workgroup's tasks
+  // only move forward, so the step is found by stepping on from the last one.
+  int g = 0;
+  int64_t lo = 0, hi = 0, sz0 = 0;
+  if (w == 0) {
+    sz0 = ld_uniform(a.mat[0].tab + 1);
+    hi = sz0 + (n1 > 0 ? ld_uniform(a.mat[1].tab + 1) : 0);
+  }
   for (;;) {
     if (w == 0) {
       // wave 0 claims the next task (lane 0's atomic, broadcast) and decodes it
@@ -539,59 +676,72 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
         tl = ab ? -1 : atomicAdd(a.ctl, 1);
       }
       tl = __builtin_amdgcn_readfirstlane(tl);
-      const int64_t t = (tl < 0 ? a.total : (int64_t)(unsigned)tl) + a.toff;
-      int kind = -1, q = 0, s = 0, i = 0, j = 0;
-      if (t < a.total + a.toff) {
-        // the step: last s with (tasks of all matrices before step s) <= t
-        const int n0 = a.mat[0].nblk, n1 = a.nmat > 1 ? a.mat[1].nblk : 0;
-        int lo = 0, hi = a.maxn - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (chol_before(n0, mid) + chol_before(n1, mid) <= t) lo = mid;
-          else hi = mid - 1;
+      const int64_t t = tl < 0 ? a.total : (int64_t)(unsigned)tl;
+      int kind = -1, q = 0, i = 0, x = 0;
+      if (t < a.total) {
+        while (t >= hi && g + 1 < a.maxn) {
+          ++g;
+          lo = hi;
+          const int g1 = g + 1;
+          const int64_t e0 = g < n0 ? ld_uniform(a.mat[0].tab + g1) : 0;
+          const int64_t b0 = g < n0 ? ld_uniform(a.mat[0].tab + g) : 0;
+          const int64_t e1 = g < n1 ? ld_uniform(a.mat[1].tab + g1) : 0;
+          const int64_t b1 = g < n1 ? ld_uniform(a.mat[1].tab + g) : 0;
+          sz0 = e0 - b0;
+          hi = lo + sz0 + (e1 - b1);
         }
-        s = lo;
-        int64_t r = t - chol_before(n0, s) - chol_before(n1, s);
-        if (s < n0 && r < chol_group_size(n0, s)) {
-          q = 0;
-        } else {
-          if (s < n0) r -= chol_group_size(n0, s);
+        int64_t r = t - lo;
+        if (r >= sz0) {
+          r -= sz0;
           q = 1;
         }
         const int n = q == 0 ? n0 : n1;
         int k = (int)r;
-        const int c1 = s >= 1 ? n - s - 1 : 0, c2 = n - s;
+        const int c1 = g >= 1 ? n - g - 1 : 0, c2 = n - g;
+        const int64_t cg = chol_group_size(n, g);
         if (k < c1) {
           kind = 0;
-          i = s + 1 + k;
-          j = s + 1;
+          i = g + 1 + k;
+          x = (g << 16) | (g + 1);
         } else if (k < c1 + c2) {
           kind = 1;
-          i = s + (k - c1);
-        } else {
+          i = g + (k - c1);
+          x = g << 16;
+        } else if (k < cg) {
           kind = 0;
           k -= c1 + c2;
-          j = s + 2;
+          int j = g + 2;
           while (k >= n - j && j < n) {
             k -= n - j;
             ++j;
           }
           i = j + k;
+          x = (g << 16) | j;
+        } else {
+          kind = 2;
+          k -= (int)cg;
+          int jj = 0;
+          while (jj < n && k >= xrow_count(n, g, jj)) {  // (k < the group's xrow tasks)
+            k -= xrow_count(n, g, jj);
+            ++jj;
+          }
+          i = g + kInvStride * jj;
+          x = (k << 16) | jj;  // s = k
         }
       }
       if (lane == 0) {
         task[0] = kind;
         task[1] = q;
         task[2] = i;
-        task[3] = (s << 16) | j;
+        task[3] = x;
       }
     }
     __syncthreads();
     const int kind = __builtin_amdgcn_readfirstlane(task[0]);
     const int q = __builtin_amdgcn_readfirstlane(task[1]);
     const int i = __builtin_amdgcn_readfirstlane(task[2]);
-    const int sj = __builtin_amdgcn_readfirstlane(task[3]);
-    const int s = sj >> 16, j = sj & 0xFFFF;
+    const int x = __builtin_amdgcn_readfirstlane(task[3]);
+    const int s = x >> 16, j = x & 0xFFFF;  // kind 2: s = column tile, j = chunk index
     __syncthreads();  // task[] is rewritten by the next claim
     if (kind < 0) return;
     // select the matrix with branches (a runtime index into the kernel argument would
@@ -599,73 +749,59 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
     const CholMat m = q == 0 ? a.mat[0] : a.mat[1];
     const int64_t p = m.p;
     const int n = m.nblk;
+    const int khi = i - kInvDepth * j, nch = xrow_chunks(i, s);
     // dependencies (wave 0 waits, the barrier releases the others)
     if (w == 0) {
-      // the panel tiles this task reads are final (kFinal), and its own tiles carry panels
-      // 0 .. s - 2; every task polls only the few tiles it reads, so the waiters of one
-      // step spread over many words
+      // every task polls only the few tiles it reads, so the waiters of one step spread
+      // over many words
       const int* tc = m.tile_cnt;
-      const int r2 = kind == 0 ? j : s;  // the second panel row read
       bool ok = true;
-      if (s >= 1) {
-        ok = chol_wait(tc + (int64_t)i * n + (s - 1), kFinal, a.ctl, a.info);
-        if (ok && r2 != i) ok = chol_wait(tc + (int64_t)r2 * n + (s - 1), kFinal, a.ctl, a.info);
-      }
-      if (ok && kind == 0) ok = chol_wait(tc + (int64_t)i * n + j, s - 1, a.ctl, a.info);
-      if (ok && kind == 1 && s >= 2) {
-        ok = chol_wait(tc + (int64_t)s * n + s, s - 1, a.ctl, a.info);
-        if (ok && i != s) ok = chol_wait(tc + (int64_t)i * n + s, s - 1, a.ctl, a.info);
+      if (kind == 2) {
+        // L_i,khi-1 final (so every L_ik, k < khi), X_khi-1,s final (so every X_ks,
+        // s <= k < khi), the previous chunks of this tile, and X_ii for the last chunk
+        ok = chol_wait(tc + (int64_t)i * n + (khi - 1), kFinal, a.ctl, a.info);
+        if (ok)
+          ok = chol_wait(khi - 1 == s ? tc + (int64_t)s * n + s : m.xcnt + (int64_t)(khi - 1) * n + s,
+                         kFinal, a.ctl, a.info);
+        if (ok && j < nch - 1)
+          ok = chol_wait(m.xcnt + (int64_t)i * n + s, nch - 1 - j, a.ctl, a.info);
+        if (ok && j == 0) ok = chol_wait(tc + (int64_t)i * n + i, kFinal, a.ctl, a.info);
+      } else {
+        // the panel tiles this task reads are final (kFinal), and its own tiles carry
+        // panels 0 .. s - 2
+        const int r2 = kind == 0 ? j : s;  // the second panel row read
+        if (s >= 1) {
+          ok = chol_wait(tc + (int64_t)i * n + (s - 1), kFinal, a.ctl, a.info);
+          if (ok && r2 != i) ok = chol_wait(tc + (int64_t)r2 * n + (s - 1), kFinal, a.ctl, a.info);
+        }
+        if (ok && kind == 0) ok = chol_wait(tc + (int64_t)i * n + j, s - 1, a.ctl, a.info);
+        if (ok && kind == 1 && s >= 2) {
+          ok = chol_wait(tc + (int64_t)s * n + s, s - 1, a.ctl, a.info);
+          if (ok && i != s) ok = chol_wait(tc + (int64_t)i * n + s, s - 1, a.ctl, a.info);
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __syncthreads();
     if (kind == 0)
-      chol_bulk<true>(p, s - 1, i, j, m.Ar, sh.t);
+      chol_bulk(p, s - 1, i, j, m.Ar, m.Lt, sh.t);
+    else if (kind == 1)
+      chol_crit(p, s, i, m.Ar, m.X, m.Lt, m.Xt, a.info, m.side_code, sh.b);
     else
-      chol_crit<true>(p, s, i, m.Ar, m.X, a.info, m.side_code, sh.b);
+      chol_xchunk(p, i, s, khi - kInvDepth > s ? khi - kInvDepth : s, khi, j == nch - 1, j == 0,
+                  m.X, m.Lt, m.Xt, sh.b);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (w == 0 && lane == 0)
-      __hip_atomic_store(m.tile_cnt + (int64_t)i * n + (kind == 0 ? j : s), kind == 0 ? s : kFinal,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (w == 0 && lane == 0) {
+      if (kind == 2)
+        __hip_atomic_store(m.xcnt + (int64_t)i * n + s, j == 0 ? kFinal : nch - j,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        __hip_atomic_store(m.tile_cnt + (int64_t)i * n + (kind == 0 ? j : s),
+                           kind == 0 ? s : kFinal, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-}
-
-// Recursive doubling, step 1: T = L21 X11 for every pair of h-blocks (group z).
-// X11 is lower triangular, so column tile tj only needs k >= 64*tj.
-__global__ __launch_bounds__(256) void k_trtri_step1(int64_t p, int64_t h, int zoff,
-                                                     const double* Ar, const double* X, double* Tb,
-                                                     int64_t ldt) {
-  __shared__ TileSmem<double> sm;
-  const int64_t g0 = (int64_t)(blockIdx.z + zoff) * 2 * h;
-  const int64_t h1 = (p - g0) < h ? (p - g0) : h;
-  const int64_t h2 = (p - g0 - h) < h ? (p - g0 - h) : h;
-  const int64_t ti = blockIdx.y, tj = blockIdx.x;
-  if (h2 <= 0 || ti * NB >= h2 || tj * NB >= h1) return;
-  const int M = (h2 - ti * NB) < NB ? (int)(h2 - ti * NB) : NB;
-  const int N = (h1 - tj * NB) < NB ? (int)(h1 - tj * NB) : NB;
-  const int64_t rA = g0 + h + ti * NB;
-  tile_gemm<double, false, false>(Ar + rA * p + g0, p, X + g0 * p + g0 + tj * NB, p,
-                                  Tb + rA * ldt + tj * NB, ldt, M, N, (int)(tj * NB), (int)h1, 1.0,
-                                  0.0, sm);
-}
-
-// Step 2: X21 = -X22 T.  X22 is lower triangular, so row tile ti only needs k < 64*(ti+1).
-__global__ __launch_bounds__(256) void k_trtri_step2(int64_t p, int64_t h, int zoff, double* X,
-                                                     const double* Tb, int64_t ldt) {
-  __shared__ TileSmem<double> sm;
-  const int64_t g0 = (int64_t)(blockIdx.z + zoff) * 2 * h;
-  const int64_t h1 = (p - g0) < h ? (p - g0) : h;
-  const int64_t h2 = (p - g0 - h) < h ? (p - g0 - h) : h;
-  const int64_t ti = blockIdx.y, tj = blockIdx.x;
-  if (h2 <= 0 || ti * NB >= h2 || tj * NB >= h1) return;
-  const int M = (h2 - ti * NB) < NB ? (int)(h2 - ti * NB) : NB;
-  const int N = (h1 - tj * NB) < NB ? (int)(h1 - tj * NB) : NB;
-  const int64_t rA = g0 + h + ti * NB;
-  const int kend = (int)((ti + 1) * NB < h2 ? (ti + 1) * NB : h2);
-  tile_gemm<double, false, false>(X + rA * p + g0 + h, p, Tb + (g0 + h) * ldt + tj * NB, ldt,
-                                  X + rA * p + g0 + tj * NB, p, M, N, 0, kend, -1.0, 0.0, sm);
 }
 
 // U'[i][j] = X[p-1-i][p-1-j] / X[p-1-i][p-1-i] for i <= j, zero below the diagonal.
@@ -686,38 +822,40 @@ __global__ __launch_bounds__(256) void k_finalize(int64_t p, const double* __res
 struct FactorWs {
   double* Ar;
   double* X;
-  double* Tb;
-  int64_t ldt;
-  double* Tt;  // the top doubling level's T (rows ldt .. p-1, ldt wide): computed while the
-               // lower levels of the trailing block, which reuse Tb, are still to come
-  int* sync;   // persistent Cholesky: control words, then its counters (chol_sync_ints)
+  double* Lt;  // the Cholesky's tiled copy of the final off-diagonal tiles of L
+  double* Xt;  // the tiled copy of the final tiles of X
+  int* sync;   // persistent kernel: control words, counters, task table (chol_sync_ints)
 };
 
-// ints of the persistent Cholesky's sync area: 64 control words, then the tile counters
+// ints of the persistent kernel's sync area: 64 control words, the tile counters of L and
+// of X, then the task table
 int64_t chol_sync_ints(int64_t p) {
   const int64_t nb = cdiv(p, NB);
-  return 64 + nb * nb;
+  return 64 + 2 * nb * nb + nb + 1;
 }
 
-// Largest half-size used by the recursive doubling (the leading dimension of T).
-int64_t trtri_ldt(int64_t p) {
-  int64_t h = NB;
-  while (2 * h < p) h *= 2;
-  return h;
+// Bytes of Lt (the strictly lower 64 x 64 tiles, nb (nb - 1) / 2) and of Xt (the lower
+// tiles with the diagonal, nb (nb + 1) / 2).
+size_t lt_bytes(int64_t p) {
+  const int64_t nb = cdiv(p, NB);
+  return (size_t)(nb * (nb - 1) / 2 > 0 ? nb * (nb - 1) / 2 : 1) * NB * NB * sizeof(double);
+}
+size_t xt_bytes(int64_t p) {
+  const int64_t nb = cdiv(p, NB);
+  return (size_t)(nb * (nb + 1) / 2) * NB * NB * sizeof(double);
 }
 
 FactorWs carve(int64_t p, void* ws) {
   FactorWs f;
   char* c = (char*)ws;
-  f.ldt = trtri_ldt(p);
   f.Ar = (double*)c;
   c += align_up((size_t)p * p * sizeof(double));
   f.X = (double*)c;
   c += align_up((size_t)p * p * sizeof(double));
-  f.Tb = (double*)c;
-  c += align_up((size_t)p * f.ldt * sizeof(double));
-  f.Tt = (double*)c;
-  c += align_up((size_t)(p > f.ldt ? p - f.ldt : 1) * f.ldt * sizeof(double));
+  f.Lt = (double*)c;
+  c += align_up(lt_bytes(p));
+  f.Xt = (double*)c;
+  c += align_up(xt_bytes(p));
   f.sync = (int*)c;
   return f;
 }
@@ -725,13 +863,12 @@ FactorWs carve(int64_t p, void* ws) {
 }  // namespace
 
 size_t factor_workspace(int64_t p) {
-  const int64_t ldt = trtri_ldt(p);
-  return 2 * align_up((size_t)p * p * sizeof(double)) + align_up((size_t)p * ldt * sizeof(double)) +
-         align_up((size_t)(p > ldt ? p - ldt : 1) * ldt * sizeof(double)) +
-         align_up((size_t)chol_sync_ints(p) * sizeof(int));
+  return 2 * align_up((size_t)p * p * sizeof(double)) + align_up(lt_bytes(p)) +
+         align_up(xt_bytes(p)) + align_up((size_t)chol_sync_ints(p) * sizeof(int));
 }
 
-// Dense GEMM flops of one launch (only evaluated while the measurement hook is on).
+// Dense GEMM flops of the trailing update by panel kb (only evaluated while the
+// measurement hook is on).
 double trailing_flops(int64_t p, int kb) {
   const int64_t nblk = cdiv(p, NB);
   const double K = (double)((p - kb * NB) < NB ? (p - kb * NB) : NB);
@@ -746,28 +883,10 @@ double trailing_flops(int64_t p, int kb) {
   return f;
 }
 
-void trtri_flops(int64_t p, int64_t h, double* f1, double* f2) {
-  *f1 = *f2 = 0.0;
-  for (int64_t g0 = 0; g0 < p; g0 += 2 * h) {
-    const int64_t h1 = (p - g0) < h ? (p - g0) : h;
-    const int64_t h2 = (p - g0 - h) < h ? (p - g0 - h) : h;
-    if (h2 <= 0) continue;
-    for (int64_t ti = 0; ti * NB < h2; ++ti) {
-      const double M = (double)((h2 - ti * NB) < NB ? (h2 - ti * NB) : NB);
-      const double kend = (double)((ti + 1) * NB < h2 ? (ti + 1) * NB : h2);
-      for (int64_t tj = 0; tj * NB < h1; ++tj) {
-        const double N = (double)((h1 - tj * NB) < NB ? (h1 - tj * NB) : NB);
-        *f1 += 2.0 * M * N * (double)(h1 - tj * NB);
-        *f2 += 2.0 * M * N * kend;
-      }
-    }
-  }
-}
-
 namespace {
 
-// The launches of one factorisation, in order: reversal, one per Cholesky step, one per
-// doubling level of the inverse (two kernels), finalisation.
+// The launches of one factorisation around its persistent kernel: reversal (stage 0),
+// finalisation (stage 1).
 struct FactorPlan {
   int64_t p;
   int dtype;
@@ -777,46 +896,22 @@ struct FactorPlan {
   int* info;
   int side_code;
   hipStream_t s;
-  int nblk, nlev;
-  int stages() const { return 1 + nblk + nlev + 1; }
+  int nblk;
 };
 
 FactorPlan plan(int64_t p, int dtype, const void* A, void* U, void* ws, int* info, int side_code,
                 hipStream_t s) {
-  FactorPlan q{p, dtype, A, U, carve(p, ws), info, side_code, s, (int)cdiv(p, NB), 0};
-  for (int64_t h = NB; h < p; h *= 2) ++q.nlev;
-  return q;
-}
-
-// One doubling level of the inverse over the groups [z0, z1) of width 2h: step 1
-// (T = L21 X11) if bit 0 of `steps` is set, step 2 (X21 = -X22 T) if bit 1 is.  The top
-// level (h == ldt) keeps T in its own buffer.
-void trtri_level(const FactorPlan& q, int64_t h, int z0, int z1, int steps) {
-  if (z1 <= z0) return;
-  const int64_t p = q.p;
-  FactorWs f = q.f;
-  // (T rows are addressed by their absolute index g0 + h + ..., >= ldt at the top level)
-  if (h == f.ldt) f.Tb = (double*)((char*)f.Tt - (size_t)f.ldt * f.ldt * sizeof(double));
-  const dim3 g((unsigned)cdiv(h, NB), (unsigned)cdiv(h, NB), (unsigned)(z1 - z0));
-  double f1 = 0.0, f2 = 0.0;
-  if (prof_on()) trtri_flops(p, h, &f1, &f2);
-  const double frac = (double)(z1 - z0) / (double)cdiv(p, 2 * h);  // (measurement only)
-  prof_begin(KC_TRTRI, q.s);
-  if (steps & 1) k_trtri_step1<<<g, 256, 0, q.s>>>(p, h, z0, f.Ar, f.X, f.Tb, f.ldt);
-  if (steps & 2) k_trtri_step2<<<g, 256, 0, q.s>>>(p, h, z0, f.X, f.Tb, f.ldt);
-  prof_end(KC_TRTRI, q.s, frac * (((steps & 1) ? f1 : 0.0) + ((steps & 2) ? f2 : 0.0)),
-           frac * 8.0 * 2.0 * (double)h * (double)p * (((steps & 1) ? 1 : 0) + ((steps & 2) ? 1 : 0)));
+  return FactorPlan{p, dtype, A, U, carve(p, ws), info, side_code, s, (int)cdiv(p, NB)};
 }
 
 void stage(const FactorPlan& q, int idx) {
   const int64_t p = q.p;
-  const bool pr = prof_on();
   const double es = q.dtype == 0 ? 4.0 : 8.0, pp = (double)p * (double)p;
   hipStream_t s = q.s;
   const FactorWs& f = q.f;
   const dim3 eg((unsigned)cdiv(p, 64), (unsigned)cdiv(p, 4));
+  prof_begin(KC_OTHER, s);
   if (idx == 0) {
-    prof_begin(KC_OTHER, s);
     if (q.dtype == 0)
       k_reverse_sym<float><<<eg, 256, 0, s>>>(p, (const float*)q.A, f.Ar);
     else
@@ -824,30 +919,6 @@ void stage(const FactorPlan& q, int idx) {
     prof_end(KC_OTHER, s, 0.0, pp * (es + 8.0));
     return;
   }
-  if (idx <= q.nblk) {
-    const int st = idx - 1;
-    const int crit = q.nblk - st, rest = q.nblk - st - 1;
-    const unsigned grid = (unsigned)(crit + (st > 0 ? rest * rest : 0));
-    double fl = 0.0, by = 0.0;
-    if (pr) {
-      const double nv = (double)((p - st * NB) < NB ? (p - st * NB) : NB);
-      const double rows = (double)(p - (int64_t)st * NB) - nv;
-      fl = 2.0 / 3.0 * nv * nv * nv + 2.0 * rows * nv * nv +
-           (st > 0 ? trailing_flops(p, st - 1) : 0.0);
-      const double trail = st > 0 ? (rows + nv) * (rows + nv + NB) / 2.0 : 0.0;
-      by = 8.0 * (3.0 * (rows + nv) * NB + 3.0 * trail);
-    }
-    prof_begin(KC_POTRF, s);
-    k_chol_step<<<grid, 256, 0, s>>>(p, st, f.Ar, f.X, q.info, q.side_code);
-    prof_end(KC_POTRF, s, fl, by);
-    return;
-  }
-  if (idx <= q.nblk + q.nlev) {
-    const int64_t h = (int64_t)NB << (idx - q.nblk - 1);
-    trtri_level(q, h, 0, (int)cdiv(p, 2 * h), 3);
-    return;
-  }
-  prof_begin(KC_OTHER, s);
   if (q.dtype == 0)
     k_finalize<float><<<eg, 256, 0, s>>>(p, f.X, (float*)q.U);
   else
@@ -863,16 +934,14 @@ __global__ __launch_bounds__(256) void k_zero_ints(int* p, int64_t n) {
     p[i] = 0;
 }
 
-// Steps [s0, s1) of the Cholesky of one or two matrices (plans qs[0..nmat)) as one
-// persistent launch on s, on at most `per_cu` workgroups per CU.  The first launch
-// (s0 == 0) clears the counters; a later one only the task counter and abort flag.
-hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int s0, int s1,
-                                   int per_cu, int* info, hipStream_t s) {
+// The Cholesky and the inverse of one or two matrices (plans qs[0..nmat)) as one
+// persistent launch on s, on at most `per_cu` workgroups per CU.
+hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int per_cu, int* info,
+                                   hipStream_t s) {
   CholArgs a{};
   a.nmat = nmat;
   a.maxn = 0;
   a.total = 0;
-  a.toff = 0;
   double fl = 0.0, by = 0.0;
   const bool pr = prof_on();
   for (int q = 0; q < nmat; ++q) {
@@ -883,22 +952,35 @@ hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int s0
     a.mat[q].side_code = pl.side_code;
     a.mat[q].Ar = pl.f.Ar;
     a.mat[q].X = pl.f.X;
+    a.mat[q].Lt = pl.f.Lt;
+    a.mat[q].Xt = pl.f.Xt;
     a.mat[q].tile_cnt = pl.f.sync + 64;
+    a.mat[q].xcnt = pl.f.sync + 64 + (int64_t)nb * nb;
+    int* tab = pl.f.sync + 64 + 2 * (int64_t)nb * nb;
+    a.mat[q].tab = tab;
     a.maxn = nb > a.maxn ? nb : a.maxn;
-    a.total += chol_before(nb, s1) - chol_before(nb, s0);
-    a.toff += chol_before(nb, s0);
-    const int64_t words = s0 == 0 ? chol_sync_ints(pl.p) : (q == 0 ? 64 : 0);
+    for (int g = 0; g < nb; ++g) a.total += group_size(nb, g);
+    const int64_t words = 64 + 2 * (int64_t)nb * nb;
     const int64_t zg = cdiv(words, 256) < 1024 ? cdiv(words, 256) : 1024;
-    if (words > 0) k_zero_ints<<<(unsigned)zg, 256, 0, s>>>(pl.f.sync, words);
+    k_zero_ints<<<(unsigned)zg, 256, 0, s>>>(pl.f.sync, words);
+    k_chol_table<<<1, 64, 0, s>>>(tab, nb);
     if (pr) {
       const int64_t p = pl.p;
-      for (int st = s0; st < (s1 < nb ? s1 : nb); ++st) {
+      for (int st = 0; st < nb; ++st) {
         const double nv = (double)((p - st * NB) < NB ? (p - st * NB) : NB);
         const double rows = (double)(p - (int64_t)st * NB) - nv;
         fl += 2.0 / 3.0 * nv * nv * nv + 2.0 * rows * nv * nv +
               (st > 0 ? trailing_flops(p, st - 1) : 0.0);
         const double trail = st > 0 ? (rows + nv) * (rows + nv + NB) / 2.0 : 0.0;
         by += 8.0 * (3.0 * (rows + nv) * NB + 3.0 * trail);
+      }
+      // row inverse: X_is = -X_ii sum_k L_ik X_ks over the tiles below the diagonal
+      for (int i = 1; i < nb; ++i) {
+        const double M = (double)((p - (int64_t)i * NB) < NB ? (p - (int64_t)i * NB) : NB);
+        for (int sc = 0; sc < i; ++sc) {
+          fl += 2.0 * M * NB * NB * (double)(i - sc + 1);
+          by += 8.0 * (2.0 * NB * NB * (double)(i - sc) + 2.0 * M * NB * xrow_chunks(i, sc));
+        }
       }
     }
   }
@@ -914,9 +996,9 @@ hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int s0
     return e;
   if (occ < 1) return hipErrorInvalidConfiguration;
   if (occ > per_cu) occ = per_cu;
-  prof_begin(KC_POTRF, s);
+  prof_begin(KC_FACTOR, s);
   k_chol_persistent<<<ncu * occ, 256, 0, s>>>(a);
-  prof_end(KC_POTRF, s, fl, by);
+  prof_end(KC_FACTOR, s, fl, by);
   return hipGetLastError();
 }
 
@@ -925,22 +1007,17 @@ hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws
   const FactorPlan q = plan(p, dtype, A, U, ws, info, side_code, s);
   stage(q, 0);
   const FactorPlan* qs[1] = {&q};
-  hipError_t e = chol_persistent_enqueue(qs, 1, 0, q.nblk, 2, info, s);
+  hipError_t e = chol_persistent_enqueue(qs, 1, 2, info, s);
   if (e != hipSuccess) return e;
-  for (int i = q.nblk + 1; i < q.stages(); ++i) stage(q, i);
+  stage(q, 1);
   return hipGetLastError();
 }
 
 hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, hipStream_t sa,
                                int64_t n, const void* B, void* Ub, void* ws_b, hipStream_t sb,
                                int dtype, int* info) {
-  // Reversal of each on its stream; both Cholesky factorisations together in persistent
-  // launches on sa; the inverses and the finalisation of each on its stream again.  The
-  // Cholesky is split at step S = H / 64, H = the inverse's top-level half-size: once
-  // block columns < S are final, the inverse of the leading H x H block and the product
-  // T = L21 X11 of the top level need nothing else, so they run on sb while the rest of
-  // the Cholesky (a dependency chain that leaves most CUs idle) runs on sa with one
-  // workgroup per CU.
+  // The reversal of each on its stream; the Cholesky and the inverse of both together in
+  // one persistent launch on sa; the finalisation of each on its stream again.
   const FactorPlan qa = plan(m, dtype, A, Ua, ws_a, info, 1, sa);
   const FactorPlan qb = plan(n, dtype, B, Ub, ws_b, info, 2, sb);
   hipStream_t aux = nullptr;
@@ -952,47 +1029,11 @@ hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, h
   if ((e = hipEventRecord(ev[3], sb)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(sa, ev[3], 0)) != hipSuccess) return e;
   const FactorPlan* qs[2] = {&qa, &qb};
-  const FactorPlan* pl[2] = {&qa, &qb};
-  const int maxn = qa.nblk > qb.nblk ? qa.nblk : qb.nblk;
-  // split step: the smallest H / 64 of the matrices that have an inverse to compute
-  int S = maxn;
-  for (int k = 0; k < 2; ++k)
-    if (pl[k]->nlev > 0 && (int)(pl[k]->f.ldt / NB) < S) S = (int)(pl[k]->f.ldt / NB);
-  bool early[2];
-  for (int k = 0; k < 2; ++k) early[k] = pl[k]->nlev > 0 && pl[k]->f.ldt / NB <= S && S < maxn;
-  if ((e = chol_persistent_enqueue(qs, 2, 0, S, 2, info, sa)) != hipSuccess) return e;
+  if ((e = chol_persistent_enqueue(qs, 2, 2, info, sa)) != hipSuccess) return e;
   if ((e = hipEventRecord(ev[2], sa)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(sb, ev[2], 0)) != hipSuccess) return e;
-  // sb: the leading blocks' inverse levels and the top level's step 1 of each matrix
-  for (int k = 0; k < 2; ++k) {
-    if (!early[k]) continue;
-    FactorPlan q = *pl[k];
-    q.s = sb;
-    const int64_t H = q.f.ldt;
-    for (int64_t h = NB; h < H; h *= 2) trtri_level(q, h, 0, (int)(H / (2 * h)), 3);
-    trtri_level(q, H, 0, 1, 1);
-  }
-  if ((e = hipEventRecord(ev[4], sb)) != hipSuccess) return e;
-  if (S < maxn) {
-    if ((e = chol_persistent_enqueue(qs, 2, S, maxn, 1, info, sa)) != hipSuccess) return e;
-  }
-  if ((e = hipEventRecord(ev[5], sa)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(sa, ev[4], 0)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(sb, ev[5], 0)) != hipSuccess) return e;
-  // the rest of each inverse and the finalisation, A on sa and B on sb
-  for (int k = 0; k < 2; ++k) {
-    FactorPlan q = *pl[k];
-    q.s = k == 0 ? sa : sb;
-    if (early[k]) {
-      const int64_t H = q.f.ldt;
-      for (int64_t h = NB; h < H; h *= 2)
-        trtri_level(q, h, (int)(H / (2 * h)), (int)cdiv(q.p, 2 * h), 3);
-      trtri_level(q, H, 0, 1, 2);
-    } else {
-      for (int i = q.nblk + 1; i <= q.nblk + q.nlev; ++i) stage(q, i);
-    }
-    stage(q, q.nblk + q.nlev + 1);
-  }
+  stage(qa, 1);
+  stage(qb, 1);
   return hipGetLastError();
 }
 

@@ -18,8 +18,8 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 std::recursive_mutex& lib_mutex();
 hipError_t aux_resources(size_t nevents, hipStream_t* aux, hipEvent_t** events);
 // events of the pool: 0, 1 join the caller's stream and the second stream around the
-// factors (api.hip), 2 .. 5 order the factor stage's launches across the two streams
-constexpr size_t kAuxEvents = 6;
+// factors (api.hip), 2, 3 order the factor stage's launches across the two streams
+constexpr size_t kAuxEvents = 4;
 
 // Factor stage (factor.hip): U' (dtype) of one SPD matrix A (dtype), fp64 inside.
 size_t factor_workspace(int64_t p);

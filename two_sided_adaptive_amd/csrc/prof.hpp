@@ -12,10 +12,9 @@ enum KernelClass : int {
   KC_SWEEP = 0,      // the persistent sweep kernel: rounding, band updates, outputs
   KC_BAND_GEMM = 1,  // band-update tasks inside the sweep (busy time of the workgroups
                      // that ran them, in CU-milliseconds; one "launch" per task)
-  KC_POTRF = 2,      // one Cholesky step of the factor stage
-  KC_TRTRI = 3,      // triangular-inverse doubling GEMMs
-  KC_OTHER = 4,      // reverse/finalize/init/check kernels
-  KC_COUNT = 5
+  KC_FACTOR = 2,     // the persistent Cholesky + inverse kernel of the factor stage
+  KC_OTHER = 3,      // reverse/finalize/init/check kernels
+  KC_COUNT = 4
 };
 
 bool prof_on();
