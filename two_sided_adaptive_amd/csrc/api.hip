@@ -71,45 +71,6 @@ void prof_end(int cls, hipStream_t s, double flops, double bytes) {
   p.open[cls] = nullptr;
 }
 
-// per-device second stream and event pool
-namespace {
-struct DeviceRes {
-  hipStream_t aux = nullptr;
-  std::vector<hipEvent_t> events;
-};
-std::vector<DeviceRes>& device_res() {
-  static std::vector<DeviceRes> v;
-  return v;
-}
-}  // namespace
-
-std::recursive_mutex& lib_mutex() {
-  static std::recursive_mutex mu;
-  return mu;
-}
-
-hipError_t aux_resources(size_t nevents, hipStream_t* aux, hipEvent_t** events) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::vector<DeviceRes>& all = device_res();
-  if ((int)all.size() <= dev) all.resize(dev + 1);
-  DeviceRes& r = all[dev];
-  if (r.aux == nullptr) {
-    e = hipStreamCreateWithFlags(&r.aux, hipStreamNonBlocking);
-    if (e != hipSuccess) return e;
-  }
-  while (r.events.size() < nevents) {
-    hipEvent_t ev;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
-    r.events.push_back(ev);
-  }
-  *aux = r.aux;
-  *events = r.events.data();
-  return hipSuccess;
-}
-
 }  // namespace g2d
 
 namespace {
@@ -254,19 +215,9 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
   c += align_up((size_t)n * n * es);
   void* scratch = c;
   void* scratch_b = c + g2d::factor_workspace(m);
-  // The factors: one persistent Cholesky launch for both on the caller's stream, B's
-  // reversal, inverse and finalisation on the library's second stream; the sweep waits
-  // for both streams.
-  std::lock_guard<std::recursive_mutex> lock(g2d::lib_mutex());
-  hipStream_t s1 = nullptr;
-  hipEvent_t* ev = nullptr;
-  hipError_t e = g2d::aux_resources(g2d::kAuxEvents, &s1, &ev);
-  if (e == hipSuccess) e = hipEventRecord(ev[0], s);
-  if (e == hipSuccess) e = hipStreamWaitEvent(s1, ev[0], 0);
-  if (e == hipSuccess)
-    e = g2d::factor_pair_enqueue(m, A, Ua, scratch, s, n, B, Ub, scratch_b, s1, dtype, info);
-  if (e == hipSuccess) e = hipEventRecord(ev[1], s1);
-  if (e == hipSuccess) e = hipStreamWaitEvent(s, ev[1], 0);
+  // Both factors in one persistent launch, then the sweep, on the caller's stream.
+  hipError_t e =
+      g2d::factor_pair_enqueue(m, A, Ua, scratch, n, B, Ub, scratch_b, dtype, info, s);
   if (e == hipSuccess)
     e = g2d::sweep_enqueue(m, n, bits, dtype, W, Ua, Ub, scales, codes, Q, scratch, info, s);
   return status(e);

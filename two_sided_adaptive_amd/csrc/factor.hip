@@ -25,18 +25,6 @@ namespace {
 
 constexpr int NB = 64;  // panel width = tile edge
 
-// Ar[i][j] = A[p-1-min(i,j)][p-1-max(i,j)]: the reversed matrix, filled symmetric from
-// the lower triangle of A.
-template <typename T>
-__global__ __launch_bounds__(256) void k_reverse_sym(int64_t p, const T* __restrict__ A,
-                                                     double* __restrict__ Ar) {
-  const int64_t j = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
-  const int64_t i = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (i >= p || j >= p) return;
-  const int64_t a = i > j ? i : j, b = i > j ? j : i;
-  Ar[i * p + j] = (double)A[(p - 1 - b) * p + (p - 1 - a)];
-}
-
 // Quad broadcast of a double: every lane of a quad receives lane `src`'s value.
 __device__ inline double quad_bcast(double v, int src) {
   // quad_perm [src, src, src, src] on both 32-bit halves (src is a literal after unrolling)
@@ -256,16 +244,37 @@ __device__ inline int tile_rows(int64_t p, int i) {
   return (p - (int64_t)i * NB) < NB ? (int)(p - (int64_t)i * NB) : NB;
 }
 
+// Element (r, c) of the reversed matrix J A J, read from the lower triangle of the input
+// A (fp32 or fp64, never written): A[p-1-min(r,c)][p-1-max(r,c)], zero past the matrix.
+// The tasks that touch a tile first read it this way, so no reversed copy is made.
+__device__ inline double ld_src(const void* A, bool f32, int64_t p, int64_t r, int64_t c) {
+  if (r >= p || c >= p) return 0.0;
+  const int64_t a = r > c ? r : c, b = r > c ? c : r;
+  const int64_t idx = (p - 1 - b) * p + (p - 1 - a);
+  return f32 ? (double)((const float*)A)[idx] : ((const double*)A)[idx];
+}
+// U'[a][b] of the output factor in its dtype
+__device__ inline void st_u(void* U, bool f32, int64_t idx, double v) {
+  if (f32)
+    ((float*)U)[idx] = (float)v;
+  else
+    ((double*)U)[idx] = v;
+}
+
 // The trailing update of one tile by one panel: A_ij -= L_ik L_jk^T (64 x 64 tiles of the
 // reversed matrix, k = panel block column).
 __device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar, const double* Lt,
-                                 TileSmem<double>& sm) {
+                                 const void* A, bool f32, TileSmem<double>& sm) {
   const int64_t ri = (int64_t)i * NB, cj = (int64_t)j * NB;
   const int M = tile_rows(p, i), N = tile_rows(p, j);
   // both operands i-major 64 x 64 from Lt, staged k-major through LDS in two chunks; the
   // tile itself at device scope
   typedef Mfma<double>::acc_t acc_t;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // an opaque copy of the thread index: values derived from it are recomputed per task
+  // instead of being held (and spilled) across the persistent loop
+  int tid = threadIdx.x;
+  __asm__ volatile("" : "+v"(tid));
+  const int lane = tid & 63, w = tid >> 6;
   const int wr = w >> 1, wc = w & 1, kr = lane >> 4, cl = lane & 15;
   const rsrc_t ra = make_rsrc(lt_tile(Lt, i, k), (int64_t)M * NB * 8);
   const rsrc_t rb = make_rsrc(lt_tile(Lt, j, k), (int64_t)N * NB * 8);
@@ -291,7 +300,9 @@ __device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar, con
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = 32 * wr + 16 * a + Mfma<double>::row(lane, e), jj = 32 * wc + 16 * b + cl;
-        old[a][b][e] = ld<true>(rc, (uint32_t)((int64_t)ii * p + jj));
+        // (panel 0 is the tile's first update: the tile is read from A itself)
+        old[a][b][e] = k == 0 ? ld_src(A, f32, p, ri + ii, cj + jj)
+                              : ld<true>(rc, (uint32_t)((int64_t)ii * p + jj));
       }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -330,12 +341,14 @@ __device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar, con
 // The panel step of row tile i of block column s: subtract the previous panel's
 // contribution from the diagonal tile (s, s) and tile (i, s), factor (s, s) (every row
 // tile does this identically, so none waits for another), then the diagonal row tile
-// writes X_ss = L_ss^-1 to X and Xt and the others solve L_is = A_is X_ss^T and write it
-// to Ar and Lt.
+// writes X_ss = L_ss^-1 to Xt and the diagonal block of U', and the others solve
+// L_is = A_is X_ss^T and write it to Ar and Lt.  Steps 0 and 1 read their tiles from A
+// (no trailing update has touched them).
 // (L_ss itself is read by nothing later; other panel steps of this block column may still
 // be reading tile (s, s), so it stays.)
-__device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X, double* Lt,
-                                 double* Xt, int* info, int side_code, BlockSmem& sm) {
+__device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* Lt, double* Xt,
+                                 const void* A, void* U, bool f32, int* info, int side_code,
+                                 BlockSmem& sm) {
   constexpr bool DEV = true;
   typedef Mfma<double>::acc_t acc_t;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, cl = lane & 15, kq = lane >> 4;
@@ -355,8 +368,13 @@ __device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * w + Mfma<double>::row(lane, e), k = 16 * t + cl;
-        v[t][e] = ld<DEV>(rd, (uint32_t)(r * p + k));
-        u[t][e] = diag ? 0.0 : ld<DEV>(rp, (uint32_t)(r * p + k));
+        if (s <= 1) {
+          v[t][e] = ld_src(A, f32, p, r0 + r, r0 + k);
+          u[t][e] = diag ? 0.0 : ld_src(A, f32, p, ri + r, r0 + k);
+        } else {
+          v[t][e] = ld<DEV>(rd, (uint32_t)(r * p + k));
+          u[t][e] = diag ? 0.0 : ld<DEV>(rp, (uint32_t)(r * p + k));
+        }
       }
     if (s > 0) {
       // L_s,s-1 and L_i,s-1 from Lt (rows past the matrix read as zeros)
@@ -415,9 +433,11 @@ __device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X,
     }
     for (int idx = tid; idx < NB * NB; idx += 256) {
       const int r = idx >> 6, k = idx & 63;
-      if (r < nv && k < nv) st<DEV>(&X[(r0 + r) * p + r0 + k], sm.xf[r][k]);
       // the whole tile, padding included (identity past the matrix), for the row inverse
       st<DEV>(const_cast<double*>(xt_tile(Xt, s, s)) + idx, sm.xf[r][k]);
+      // U'[p-1-a][p-1-b] = X[a][b] / X[a][a] for b <= a, zero above (the lower U')
+      if (r < nv && k < nv)
+        st_u(U, f32, (p - 1 - r0 - r) * p + (p - 1 - r0 - k), k <= r ? sm.xf[r][k] / sm.xf[r][r] : 0.0);
     }
     return;
   }
@@ -450,14 +470,18 @@ __device__ inline void chol_crit(int64_t p, int s, int i, double* Ar, double* X,
 // Y_is = sum_{k=s}^{i-1} L_ik X_ks (from L X = I, block row i).  The sum is split into
 // chunks of at most kInvDepth tiles of k, added oldest first: this task adds the tiles
 // k in [klo, khi) to the partial sum kept in X (the first chunk starts it), and the chunk
-// that ends at k = i - 1 (last) forms X_is and writes it to X and Xt.  L_ik and X_ks come
-// from Lt and Xt through the caches; the partial sums, which other workgroups rewrite, at
-// device scope.
+// that ends at k = i - 1 (last) forms X_is, writes it to Xt and its block of U', and
+// clears the mirrored block of U'.  L_ik and X_ks come from Lt and Xt through the caches;
+// the partial sums, which other workgroups rewrite, at device scope.
 __device__ inline void chol_xchunk(int64_t p, int i, int s, int klo, int khi, bool first,
-                                   bool last, double* X, const double* Lt, double* Xt,
-                                   BlockSmem& sm) {
+                                   bool last, double* X, const double* Lt, double* Xt, void* U,
+                                   bool f32, BlockSmem& sm) {
   typedef Mfma<double>::acc_t acc_t;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // an opaque copy of the thread index: values derived from it are recomputed per task
+  // instead of being held (and spilled) across the persistent loop
+  int tid = threadIdx.x;
+  __asm__ volatile("" : "+v"(tid));
+  const int lane = tid & 63, w = tid >> 6;
   const int wr = w >> 1, wc = w & 1, kr = lane >> 4, cl = lane & 15;
   const int mi = tile_rows(p, i);
   const int64_t ri = (int64_t)i * NB, cs = (int64_t)s * NB;  // block column s is full width
@@ -535,6 +559,18 @@ __device__ inline void chol_xchunk(int64_t p, int i, int s, int klo, int khi, bo
     __syncthreads();
     mma(-1.0);
   }
+  if (!last) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = 32 * wr + 16 * a + Mfma<double>::row(lane, e), jj = 32 * wc + 16 * b + cl;
+          if (ii < mi) st<true>(&X[(ri + ii) * p + cs + jj], acc[a][b][e]);
+        }
+    return;
+  }
   double* xt = const_cast<double*>(xt_tile(Xt, i, s));
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -543,9 +579,17 @@ __device__ inline void chol_xchunk(int64_t p, int i, int s, int klo, int khi, bo
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = 32 * wr + 16 * a + Mfma<double>::row(lane, e), jj = 32 * wc + 16 * b + cl;
-        if (ii < mi) st<true>(&X[(ri + ii) * p + cs + jj], acc[a][b][e]);
-        if (last) st<true>(&xt[ii * NB + jj], acc[a][b][e]);
+        st<true>(&xt[ii * NB + jj], acc[a][b][e]);
+        // U'[p-1-a][p-1-b] = X[a][b] / X[a][a] (lf still holds X_ii)
+        if (ii < mi)
+          st_u(U, f32, (p - 1 - ri - ii) * p + (p - 1 - cs - jj), acc[a][b][e] / sm.lf[ii][ii]);
       }
+  // the mirrored block (rows of tile s, columns of tile i, reversed) lies below U''s
+  // diagonal
+  for (int idx = tid; idx < NB * NB; idx += 256) {
+    const int rr = idx >> 6, cc = idx & 63;
+    if (cc < mi) st_u(U, f32, (p - 1 - cs - rr) * p + (p - 1 - ri - cc), 0.0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -574,8 +618,11 @@ constexpr int kMaxChol = 2;
 struct CholMat {
   int64_t p;
   int nblk, side_code;
-  double* Ar;
-  double* X;
+  const void* A;   // the input matrix (lower triangle read), fp32 or fp64
+  void* U;         // the output U' in the same dtype
+  int f32;
+  double* Ar;      // the reversed matrix, updated in place; L's panels
+  double* X;       // partial sums of the row inverse
   double* Lt;      // final off-diagonal tiles of L, tiled (written once)
   double* Xt;      // final tiles of X, tiled (written once)
   int* tile_cnt;   // [nblk * nblk] panels applied to each tile by bulk tasks (kFinal: L)
@@ -614,15 +661,44 @@ __host__ __device__ inline int xrow_chunks(int i, int s) {
   return (i - s + kInvDepth - 1) / kInvDepth;
 }
 
-// tab[g] = tasks of the matrix before step g (one thread; n + 1 entries)
-__global__ __launch_bounds__(64) void k_chol_table(int* tab, int n) {
-  if (threadIdx.x != 0) return;
-  int64_t t = 0;
-  for (int g = 0; g < n; ++g) {
-    tab[g] = (int)t;
-    t += group_size(n, g);
+// Clears the control words and tile counters of up to two matrices and writes each
+// matrix's task table tab[g] = tasks of the matrix before step g (n + 1 entries).  One
+// launch: block 0 also computes the tables (group sizes in parallel, a sequential scan).
+struct CholSetup {
+  int* zero[kMaxChol];
+  int64_t words[kMaxChol];
+  int* tab[kMaxChol];
+  int n[kMaxChol];
+  int nmat;
+};
+__global__ __launch_bounds__(256) void k_chol_setup(CholSetup c) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int q = 0; q < c.nmat; ++q) {
+    int* z = q == 0 ? c.zero[0] : c.zero[1];
+    const int64_t words = q == 0 ? c.words[0] : c.words[1];
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < words; x += stride) z[x] = 0;
   }
-  tab[n] = (int)t;
+  if (blockIdx.x != 0) return;
+  __shared__ int gs[256];
+  for (int q = 0; q < c.nmat; ++q) {
+    int* tab = q == 0 ? c.tab[0] : c.tab[1];
+    const int n = q == 0 ? c.n[0] : c.n[1];
+    int run = 0;  // thread 0's running total
+    for (int base = 0; base < n; base += 256) {
+      const int g = base + (int)threadIdx.x;
+      gs[threadIdx.x] = g < n ? (int)group_size(n, g) : 0;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const int cnt = n - base < 256 ? n - base : 256;
+        for (int k = 0; k < cnt; ++k) {
+          tab[base + k] = run;
+          run += gs[k];
+        }
+        if (base + cnt == n) tab[n] = run;
+      }
+      __syncthreads();
+    }
+  }
 }
 
 // whole-wave bounded wait until *cnt >= v (false after an abort or a timeout)
@@ -783,13 +859,14 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __syncthreads();
+    const bool f32 = m.f32 != 0;
     if (kind == 0)
-      chol_bulk(p, s - 1, i, j, m.Ar, m.Lt, sh.t);
+      chol_bulk(p, s - 1, i, j, m.Ar, m.Lt, m.A, f32, sh.t);
     else if (kind == 1)
-      chol_crit(p, s, i, m.Ar, m.X, m.Lt, m.Xt, a.info, m.side_code, sh.b);
+      chol_crit(p, s, i, m.Ar, m.Lt, m.Xt, m.A, m.U, f32, a.info, m.side_code, sh.b);
     else
       chol_xchunk(p, i, s, khi - kInvDepth > s ? khi - kInvDepth : s, khi, j == nch - 1, j == 0,
-                  m.X, m.Lt, m.Xt, sh.b);
+                  m.X, m.Lt, m.Xt, m.U, f32, sh.b);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -802,21 +879,6 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
                            kind == 0 ? s : kFinal, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-}
-
-// U'[i][j] = X[p-1-i][p-1-j] / X[p-1-i][p-1-i] for i <= j, zero below the diagonal.
-template <typename T>
-__global__ __launch_bounds__(256) void k_finalize(int64_t p, const double* __restrict__ X,
-                                                  T* __restrict__ U) {
-  const int64_t j = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
-  const int64_t i = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (i >= p || j >= p) return;
-  T v = T(0);
-  if (i <= j) {
-    const int64_t a = p - 1 - i, b = p - 1 - j;
-    v = (T)(X[a * p + b] / X[a * p + a]);
-  }
-  U[i * p + j] = v;
 }
 
 struct FactorWs {
@@ -885,87 +947,61 @@ double trailing_flops(int64_t p, int kb) {
 
 namespace {
 
-// The launches of one factorisation around its persistent kernel: reversal (stage 0),
-// finalisation (stage 1).
 struct FactorPlan {
   int64_t p;
   int dtype;
   const void* A;
   void* U;
   FactorWs f;
-  int* info;
   int side_code;
-  hipStream_t s;
-  int nblk;
 };
 
-FactorPlan plan(int64_t p, int dtype, const void* A, void* U, void* ws, int* info, int side_code,
-                hipStream_t s) {
-  return FactorPlan{p, dtype, A, U, carve(p, ws), info, side_code, s, (int)cdiv(p, NB)};
-}
-
-void stage(const FactorPlan& q, int idx) {
-  const int64_t p = q.p;
-  const double es = q.dtype == 0 ? 4.0 : 8.0, pp = (double)p * (double)p;
-  hipStream_t s = q.s;
-  const FactorWs& f = q.f;
-  const dim3 eg((unsigned)cdiv(p, 64), (unsigned)cdiv(p, 4));
-  prof_begin(KC_OTHER, s);
-  if (idx == 0) {
-    if (q.dtype == 0)
-      k_reverse_sym<float><<<eg, 256, 0, s>>>(p, (const float*)q.A, f.Ar);
-    else
-      k_reverse_sym<double><<<eg, 256, 0, s>>>(p, (const double*)q.A, f.Ar);
-    prof_end(KC_OTHER, s, 0.0, pp * (es + 8.0));
-    return;
-  }
-  if (q.dtype == 0)
-    k_finalize<float><<<eg, 256, 0, s>>>(p, f.X, (float*)q.U);
-  else
-    k_finalize<double><<<eg, 256, 0, s>>>(p, f.X, (double*)q.U);
-  prof_end(KC_OTHER, s, 0.0, pp * (8.0 / 2.0 + es));
+FactorPlan plan(int64_t p, int dtype, const void* A, void* U, void* ws, int side_code) {
+  return FactorPlan{p, dtype, A, U, carve(p, ws), side_code};
 }
 
 }  // namespace
 
-// control words and counters start at zero (a fill kernel: the call may be captured)
-__global__ __launch_bounds__(256) void k_zero_ints(int* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    p[i] = 0;
-}
-
-// The Cholesky and the inverse of one or two matrices (plans qs[0..nmat)) as one
-// persistent launch on s, on at most `per_cu` workgroups per CU.
+// The factor of one or two matrices (plans qs[0..nmat)): a setup launch (counters cleared,
+// task tables) and the persistent launch, which reads A, computes L and X = L^-1 and writes
+// U', on at most `per_cu` workgroups per CU, both on s.
 hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int per_cu, int* info,
                                    hipStream_t s) {
   CholArgs a{};
-  a.nmat = nmat;
+  CholSetup su{};
+  a.nmat = su.nmat = nmat;
   a.maxn = 0;
   a.total = 0;
   double fl = 0.0, by = 0.0;
   const bool pr = prof_on();
+  int64_t words = 0;
   for (int q = 0; q < nmat; ++q) {
     const FactorPlan& pl = *qs[q];
     const int nb = (int)cdiv(pl.p, NB);
-    a.mat[q].p = pl.p;
-    a.mat[q].nblk = nb;
-    a.mat[q].side_code = pl.side_code;
-    a.mat[q].Ar = pl.f.Ar;
-    a.mat[q].X = pl.f.X;
-    a.mat[q].Lt = pl.f.Lt;
-    a.mat[q].Xt = pl.f.Xt;
-    a.mat[q].tile_cnt = pl.f.sync + 64;
-    a.mat[q].xcnt = pl.f.sync + 64 + (int64_t)nb * nb;
-    int* tab = pl.f.sync + 64 + 2 * (int64_t)nb * nb;
-    a.mat[q].tab = tab;
+    CholMat& m = a.mat[q];
+    m.p = pl.p;
+    m.nblk = nb;
+    m.side_code = pl.side_code;
+    m.A = pl.A;
+    m.U = pl.U;
+    m.f32 = pl.dtype == 0 ? 1 : 0;
+    m.Ar = pl.f.Ar;
+    m.X = pl.f.X;
+    m.Lt = pl.f.Lt;
+    m.Xt = pl.f.Xt;
+    m.tile_cnt = pl.f.sync + 64;
+    m.xcnt = pl.f.sync + 64 + (int64_t)nb * nb;
+    m.tab = pl.f.sync + 64 + 2 * (int64_t)nb * nb;
+    su.zero[q] = pl.f.sync;
+    su.words[q] = 64 + 2 * (int64_t)nb * nb;
+    su.tab[q] = pl.f.sync + 64 + 2 * (int64_t)nb * nb;
+    su.n[q] = nb;
+    words += su.words[q];
     a.maxn = nb > a.maxn ? nb : a.maxn;
     for (int g = 0; g < nb; ++g) a.total += group_size(nb, g);
-    const int64_t words = 64 + 2 * (int64_t)nb * nb;
-    const int64_t zg = cdiv(words, 256) < 1024 ? cdiv(words, 256) : 1024;
-    k_zero_ints<<<(unsigned)zg, 256, 0, s>>>(pl.f.sync, words);
-    k_chol_table<<<1, 64, 0, s>>>(tab, nb);
     if (pr) {
       const int64_t p = pl.p;
+      const double es = pl.dtype == 0 ? 4.0 : 8.0, pp = (double)p * (double)p;
       for (int st = 0; st < nb; ++st) {
         const double nv = (double)((p - st * NB) < NB ? (p - st * NB) : NB);
         const double rows = (double)(p - (int64_t)st * NB) - nv;
@@ -982,8 +1018,10 @@ hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int pe
           by += 8.0 * (2.0 * NB * NB * (double)(i - sc) + 2.0 * M * NB * xrow_chunks(i, sc));
         }
       }
+      by += pp * (es / 2.0 + es);  // A's lower triangle in, U' out
     }
   }
+  if (a.total > 0x7FFFFFFF) return hipErrorInvalidValue;  // task indices are 32-bit
   a.ctl = qs[0]->f.sync;
   a.info = info;
   int dev = 0, ncu = 0, occ = 0;
@@ -996,6 +1034,10 @@ hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int pe
     return e;
   if (occ < 1) return hipErrorInvalidConfiguration;
   if (occ > per_cu) occ = per_cu;
+  const int64_t zg = cdiv(words, 256) < 1024 ? cdiv(words, 256) : 1024;
+  prof_begin(KC_OTHER, s);
+  k_chol_setup<<<(unsigned)(zg > 0 ? zg : 1), 256, 0, s>>>(su);
+  prof_end(KC_OTHER, s, 0.0, 4.0 * (double)words);
   prof_begin(KC_FACTOR, s);
   k_chol_persistent<<<ncu * occ, 256, 0, s>>>(a);
   prof_end(KC_FACTOR, s, fl, by);
@@ -1004,37 +1046,18 @@ hipError_t chol_persistent_enqueue(const FactorPlan* const* qs, int nmat, int pe
 
 hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws, int* info,
                           int side_code, hipStream_t s) {
-  const FactorPlan q = plan(p, dtype, A, U, ws, info, side_code, s);
-  stage(q, 0);
+  const FactorPlan q = plan(p, dtype, A, U, ws, side_code);
   const FactorPlan* qs[1] = {&q};
-  hipError_t e = chol_persistent_enqueue(qs, 1, 2, info, s);
-  if (e != hipSuccess) return e;
-  stage(q, 1);
-  return hipGetLastError();
+  return chol_persistent_enqueue(qs, 1, 2, info, s);
 }
 
-hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, hipStream_t sa,
-                               int64_t n, const void* B, void* Ub, void* ws_b, hipStream_t sb,
-                               int dtype, int* info) {
-  // The reversal of each on its stream; the Cholesky and the inverse of both together in
-  // one persistent launch on sa; the finalisation of each on its stream again.
-  const FactorPlan qa = plan(m, dtype, A, Ua, ws_a, info, 1, sa);
-  const FactorPlan qb = plan(n, dtype, B, Ub, ws_b, info, 2, sb);
-  hipStream_t aux = nullptr;
-  hipEvent_t* ev = nullptr;
-  hipError_t e = aux_resources(kAuxEvents, &aux, &ev);
-  if (e != hipSuccess) return e;
-  stage(qa, 0);
-  stage(qb, 0);
-  if ((e = hipEventRecord(ev[3], sb)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(sa, ev[3], 0)) != hipSuccess) return e;
+hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, int64_t n,
+                               const void* B, void* Ub, void* ws_b, int dtype, int* info,
+                               hipStream_t s) {
+  const FactorPlan qa = plan(m, dtype, A, Ua, ws_a, 1);
+  const FactorPlan qb = plan(n, dtype, B, Ub, ws_b, 2);
   const FactorPlan* qs[2] = {&qa, &qb};
-  if ((e = chol_persistent_enqueue(qs, 2, 2, info, sa)) != hipSuccess) return e;
-  if ((e = hipEventRecord(ev[2], sa)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(sb, ev[2], 0)) != hipSuccess) return e;
-  stage(qa, 1);
-  stage(qb, 1);
-  return hipGetLastError();
+  return chol_persistent_enqueue(qs, 2, 2, info, s);
 }
 
 }  // namespace g2d
