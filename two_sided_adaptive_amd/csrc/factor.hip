@@ -605,15 +605,18 @@ __device__ inline void chol_xchunk(int64_t p, int i, int s, int klo, int khi, bo
 //            (g, g), (i, g) with panels 0 .. g - 2; afterwards (i, g) holds L_ig, final;
 //            crit(g) of i = g also writes X_gg);
 //   xrow(g): chunk jj of X_is for i = g + kInvStride jj and every s with a non-empty
-//            chunk: k in [max(s, khi - kInvDepth), khi), khi = i - kInvDepth jj (needs
-//            L_i,khi-1 and X_khi-1,s final, and the tile's previous chunk; chunk 0 also
-//            X_ii).  A row's chunks thus sit in the steps just before its own, oldest
-//            chunk first.
+//            chunk.  Chunk 0, the last one added, covers k in [i - kInvFirst, i) and
+//            multiplies by -X_ii; chunk jj >= 1 covers kInvDepth tiles below
+//            khi = i - kInvFirst - kInvDepth (jj - 1) (all clipped at s).  A chunk needs
+//            L_i,khi-1 and X_khi-1,s final and the tile's previous chunk; chunk 0 also
+//            X_ii.  A row's chunks thus sit in the steps just before its own, oldest chunk
+//            first, and the chain from one row of X to the next is one short chunk.
 // Group (q, g) lists bulk(g) of column g + 1 first, then crit(g), then the rest of
 // bulk(g) column by column, then xrow(g) by jj and s; groups go by step, the matrices
 // alternating.  Every task depends only on earlier tasks, so the queue always drains.
 constexpr int kInvDepth = 8;   // tiles of k per chunk of the row inverse
-constexpr int kInvStride = 2;  // steps between the chunks of one row
+constexpr int kInvFirst = 8;   // tiles of k of a row's last chunk
+constexpr int kInvStride = 2;  // steps between the chunks of one row (<= kInvFirst + 1)
 constexpr int kMaxChol = 2;
 struct CholMat {
   int64_t p;
@@ -645,20 +648,23 @@ __host__ __device__ inline int64_t chol_group_size(int n, int g) {
   const int64_t u = n - g;
   return g == 0 ? n : u * (u + 1) / 2;
 }
-// xrow tasks of chunk jj in group g: the columns s < g - (kInvDepth - kInvStride) jj, while
-// the row g + kInvStride jj exists.
+// xrow tasks of chunk jj in group g (row i = g + kInvStride jj): chunk 0 of every s < g;
+// for jj >= 1 the columns s < khi = g - (kInvDepth - kInvStride) jj + kInvDepth - kInvFirst
+// (a count that falls with jj).
 __host__ __device__ inline int xrow_count(int n, int g, int jj) {
-  const int cnt = g - (kInvDepth - kInvStride) * jj;
-  return (g + kInvStride * jj < n && cnt > 0) ? cnt : 0;
+  if (g + kInvStride * jj >= n) return 0;
+  if (jj == 0) return g;
+  const int cnt = g - (kInvDepth - kInvStride) * jj + kInvDepth - kInvFirst;
+  return cnt > 0 ? cnt : 0;
 }
 __host__ __device__ inline int64_t group_size(int n, int g) {
-  int64_t c = chol_group_size(n, g);
-  for (int jj = 0; xrow_count(n, g, jj) > 0; ++jj) c += xrow_count(n, g, jj);
+  int64_t c = chol_group_size(n, g) + xrow_count(n, g, 0);
+  for (int jj = 1; xrow_count(n, g, jj) > 0; ++jj) c += xrow_count(n, g, jj);
   return c;
 }
 // chunks of the row inverse of tile (i, s), i > s
 __host__ __device__ inline int xrow_chunks(int i, int s) {
-  return (i - s + kInvDepth - 1) / kInvDepth;
+  return 1 + (i - s > kInvFirst ? (i - s - kInvFirst + kInvDepth - 1) / kInvDepth : 0);
 }
 
 // Clears the control words and tile counters of up to two matrices and writes each
@@ -797,9 +803,13 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
           kind = 2;
           k -= (int)cg;
           int jj = 0;
-          while (jj < n && k >= xrow_count(n, g, jj)) {  // (k < the group's xrow tasks)
-            k -= xrow_count(n, g, jj);
-            ++jj;
+          if (k >= xrow_count(n, g, 0)) {
+            k -= xrow_count(n, g, 0);
+            jj = 1;
+            while (jj < n && k >= xrow_count(n, g, jj)) {  // (k < the group's xrow tasks)
+              k -= xrow_count(n, g, jj);
+              ++jj;
+            }
           }
           i = g + kInvStride * jj;
           x = (k << 16) | jj;  // s = k
@@ -825,7 +835,9 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
     const CholMat m = q == 0 ? a.mat[0] : a.mat[1];
     const int64_t p = m.p;
     const int n = m.nblk;
-    const int khi = i - kInvDepth * j, nch = xrow_chunks(i, s);
+    // kind 2: chunk j of tile (i, s) covers k in [klo, khi)
+    const int khi = j == 0 ? i : i - kInvFirst - kInvDepth * (j - 1), nch = xrow_chunks(i, s);
+    const int klo0 = khi - (j == 0 ? kInvFirst : kInvDepth), klo = klo0 > s ? klo0 : s;
     // dependencies (wave 0 waits, the barrier releases the others)
     if (w == 0) {
       // every task polls only the few tiles it reads, so the waiters of one step spread
@@ -860,13 +872,20 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __syncthreads();
     const bool f32 = m.f32 != 0;
+    // The panel steps are the chain that sets the launch's length, and the next block
+    // column's trailing update feeds it: their waves take the SIMDs first when they share a
+    // CU with the inverse chunks and the rest of the trailing update.
+    if (kind == 1)
+      __builtin_amdgcn_s_setprio(3);
+    else if (kind == 0 && j == s + 1)
+      __builtin_amdgcn_s_setprio(2);
     if (kind == 0)
       chol_bulk(p, s - 1, i, j, m.Ar, m.Lt, m.A, f32, sh.t);
     else if (kind == 1)
       chol_crit(p, s, i, m.Ar, m.Lt, m.Xt, m.A, m.U, f32, a.info, m.side_code, sh.b);
     else
-      chol_xchunk(p, i, s, khi - kInvDepth > s ? khi - kInvDepth : s, khi, j == nch - 1, j == 0,
-                  m.X, m.Lt, m.Xt, m.U, f32, sh.b);
+      chol_xchunk(p, i, s, klo, khi, j == nch - 1, j == 0, m.X, m.Lt, m.Xt, m.U, f32, sh.b);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
