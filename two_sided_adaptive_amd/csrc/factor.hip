@@ -72,8 +72,8 @@ struct BlockSmem {
   double xf[NB][PD];  // X = L^-1 (zeros above the diagonal)
   union {
     struct {
-      double pub[NB][4];  // the group's four columns, current values
-      double lc[NB][4];   // the group's four columns of L
+      double pub[2][NB][4];  // the group's four columns, current values (by group parity)
+      double lc[4][NB][4];   // per wave: the group's four columns of L, every row
     } g;
     double tsc[4][16][18];  // per-wave 16x16 temporaries of the inverse
   } u;
@@ -84,75 +84,80 @@ struct BlockSmem {
 // the four waves of the workgroup (wave w: rows 16w..16w+15, acc[t] the 16x16 tile of
 // columns 16t..16t+15; only the lower triangle is read; padding rows/columns hold the
 // identity).  Leaves L in sm.lf and X = L^-1 in sm.xf; ends with a barrier.
-//  * Cholesky, four columns at a time: the group's columns are published to LDS; lanes
-//    0..15 of every wave (one per row) factor the 4x4 diagonal block (redundantly) and
-//    solve their row's four L entries; the rank-4 update of the trailing tiles is one
-//    MFMA per tile.
+//  * Cholesky, four columns at a time: the group's columns are published to LDS; every
+//    wave factors the 4x4 diagonal block and solves the four L entries of all 64 rows
+//    (lane i: row i), so that it has every operand of its rank-4 update (one MFMA per
+//    tile of its own rows) in its own LDS area, and one barrier per group suffices (the
+//    published columns alternate between two buffers).
 //  * Inverse by 16x16 tiles: wave t inverts diagonal tile t by forward substitution
 //    (quad c solves column c, the new entry broadcast inside the quad with DPP); the
 //    tiles below follow by distance, X_ij = -X_ii (sum_{j<=k<i} L_ik X_kj), with MFMA.
 __device__ inline void chol_inv_block(Mfma<double>::acc_t (&acc)[4], BlockSmem& sm) {
   typedef Mfma<double>::acc_t acc_t;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, cl = lane & 15, kq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, cl = lane & 15, kq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int idx = tid; idx < NB * NB; idx += 256) sm.xf[idx >> 6][idx & 63] = 0.0;
 #pragma unroll
   for (int g = 0; g < NB / 4; ++g) {
-    const int tg = g >> 2, cg = 4 * (g & 3), d0 = 4 * g;
+    const int tg = g >> 2, cg = 4 * (g & 3), d0 = 4 * g, pb = g & 1;
     if (cl >= cg && cl < cg + 4) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        sm.u.g.pub[16 * w + Mfma<double>::row(lane, e)][cl - cg] = acc[tg][e];
+        sm.u.g.pub[pb][16 * w + Mfma<double>::row(lane, e)][cl - cg] = acc[tg][e];
     }
     __syncthreads();
-    if (lane < 16) {
-      const int i = 16 * w + lane;
-      const double(*pub)[4] = sm.u.g.pub;
+    {
+      const int i = lane;
+      const double(*pub)[4] = sm.u.g.pub[pb];
       const double b00 = pub[d0][0];
       const double b10 = pub[d0 + 1][0], b11 = pub[d0 + 1][1];
       const double b20 = pub[d0 + 2][0], b21 = pub[d0 + 2][1], b22 = pub[d0 + 2][2];
       const double b30 = pub[d0 + 3][0], b31 = pub[d0 + 3][1], b32 = pub[d0 + 3][2];
       const double b33 = pub[d0 + 3][3];
+      const double a0 = pub[i][0], a1 = pub[i][1], a2 = pub[i][2], a3 = pub[i][3];
       const double q0 = b00, s0 = rsq_nr(q0);
-      const double l00 = q0 * s0, l10 = b10 * s0, l20 = b20 * s0, l30 = b30 * s0;
+      const double l10 = b10 * s0, l20 = b20 * s0, l30 = b30 * s0;
       const double q1 = fma(-l10, l10, b11), s1 = rsq_nr(q1);
-      const double l11 = q1 * s1, l21 = fma(-l20, l10, b21) * s1, l31 = fma(-l30, l10, b31) * s1;
+      const double l21 = fma(-l20, l10, b21) * s1, l31 = fma(-l30, l10, b31) * s1;
       const double q2 = fma(-l21, l21, fma(-l20, l20, b22)), s2 = rsq_nr(q2);
-      const double l22 = q2 * s2, l32 = fma(-l31, l21, fma(-l30, l20, b32)) * s2;
+      const double l32 = fma(-l31, l21, fma(-l30, l20, b32)) * s2;
       const double q3 = fma(-l32, l32, fma(-l31, l31, fma(-l30, l30, b33))), s3 = rsq_nr(q3);
-      const double l33 = q3 * s3;
-      double x0, x1, x2, x3;
-      if (i >= d0 + 4) {
-        x0 = pub[i][0] * s0;
-        x1 = fma(-x0, l10, pub[i][1]) * s1;
-        x2 = fma(-x1, l21, fma(-x0, l20, pub[i][2])) * s2;
-        x3 = fma(-x2, l32, fma(-x1, l31, fma(-x0, l30, pub[i][3]))) * s3;
-      } else {
-        const int rr = i - d0;  // < 0 above the group: zeros
-        x0 = rr == 0 ? l00 : (rr == 1 ? l10 : (rr == 2 ? l20 : (rr == 3 ? l30 : 0.0)));
-        x1 = rr == 1 ? l11 : (rr == 2 ? l21 : (rr == 3 ? l31 : 0.0));
-        x2 = rr == 2 ? l22 : (rr == 3 ? l32 : 0.0);
-        x3 = rr == 3 ? l33 : 0.0;
+      // row i's four entries; for the group's own rows the same expressions give its L
+      // entries (the diagonal one as q * rsqrt(q)); above the diagonal they are zero
+      const int rr = i - d0;
+      double x0 = a0 * s0;
+      double x1 = fma(-x0, l10, a1) * s1;
+      double x2 = fma(-x1, l21, fma(-x0, l20, a2)) * s2;
+      double x3 = fma(-x2, l32, fma(-x1, l31, fma(-x0, l30, a3))) * s3;
+      x0 = rr >= 0 ? x0 : 0.0;
+      x1 = rr >= 1 ? x1 : 0.0;
+      x2 = rr >= 2 ? x2 : 0.0;
+      x3 = rr >= 3 ? x3 : 0.0;
+      double* lcw = sm.u.g.lc[w][i];
+      lcw[0] = x0;
+      lcw[1] = x1;
+      lcw[2] = x2;
+      lcw[3] = x3;
+      if ((i >> 4) == w) {
+        sm.lf[i][d0] = x0;
+        sm.lf[i][d0 + 1] = x1;
+        sm.lf[i][d0 + 2] = x2;
+        sm.lf[i][d0 + 3] = x3;
       }
-      sm.u.g.lc[i][0] = x0;
-      sm.u.g.lc[i][1] = x1;
-      sm.u.g.lc[i][2] = x2;
-      sm.u.g.lc[i][3] = x3;
-      sm.lf[i][d0] = x0;
-      sm.lf[i][d0 + 1] = x1;
-      sm.lf[i][d0 + 2] = x2;
-      sm.lf[i][d0 + 3] = x3;
-      if (i == 0) {
+      if (w == 0 && i == 0) {
         sm.piv[d0] = q0;
         sm.piv[d0 + 1] = q1;
         sm.piv[d0 + 2] = q2;
         sm.piv[d0 + 3] = q3;
       }
     }
-    __syncthreads();
-    // rank-4 update a[i][k] -= sum_c L[i][d0+c] L[k][d0+c] of the tiles not yet finished
-    const double af = -sm.u.g.lc[16 * w + cl][kq];
+    __asm__ volatile("" ::: "memory");  // same wave: LDS keeps program order
+    // rank-4 update a[i][k] -= sum_c L[i][d0+c] L[k][d0+c] of this wave's tiles that are
+    // not finished (columns k of tiles t in [tg, w]: the lower triangle)
+    const double af = -sm.u.g.lc[w][16 * w + cl][kq];
 #pragma unroll
-    for (int t = tg; t < 4; ++t) acc[t] = Mfma<double>::run(af, sm.u.g.lc[16 * t + cl][kq], acc[t]);
+    for (int t = tg; t < 4; ++t)
+      if (t <= w) acc[t] = Mfma<double>::run(af, sm.u.g.lc[w][16 * t + cl][kq], acc[t]);
   }
   __syncthreads();  // pub/lc are dead; tsc (same storage) is used below
   // inverse of the diagonal tile of wave w: quad c solves column c; lane q keeps the
