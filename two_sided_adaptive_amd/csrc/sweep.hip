@@ -402,12 +402,121 @@ struct BandSmem {
   int bcast[4];
 };
 
-// Rounds micro-tile (w, j) of band K and stores its R, Delta, codes and Q.
+// The loads of micro-tile (w, j) that do not depend on the phase before it: the U'b rows
+// of its local window and its diagonal U'b block (k-major B operand), W, and the feedback
+// pushed by the GEMM workers of every class (final once the block's counters are
+// complete).  A band worker issues them one phase early, before the phase barrier, so
+// that their latency passes during the barrier and the hand-over.
+template <typename T>
+struct TileLoads {
+  T win[4];
+  T vf[NCLS][4], hf[NCLS][4];
+};
+template <typename T>
+struct UbLoads {
+  T bwin[7 * MU / 4];
+  T ubd[MU * MU / 64];
+};
+// The U'b operands of micro-column j (read by every band, so mostly from L2; loaded in
+// the phase that uses them).
+template <typename T>
+__device__ inline void ub_loads(const SweepArgs<T>& a, int j, UbLoads<T>& ub) {
+  const int64_t n = a.n;
+  const int lane = threadIdx.x & 63;
+  const int kq = lane >> 4, cl = lane & 15;
+  const int64_t c0 = (int64_t)j * MU;
+  const int nc = (n - c0) < MU ? (int)(n - c0) : MU;
+  const int L = j / GOUT;
+  const int clo = GOUT * (L > 0 ? L - 1 : 0);
+  const int nwin = j - clo;
+  const int64_t es = sizeof(T);
+  const rsrc_t rb = make_rsrc(a.Ub + (int64_t)clo * MU * n + c0,
+                              nwin > 0 ? ((int64_t)(nwin * MU - 1) * n + nc) * es : 0);
+#pragma unroll
+  for (int s = 0; s < 7 * MU / 4; ++s)
+    ub.bwin[s] = buf_load<T>(rb, (uint32_t)((4 * s + kq) * n + cl));
+  const rsrc_t rd = make_rsrc(a.Ub + c0 * n + c0, ((int64_t)(nc - 1) * n + nc) * es);
+#pragma unroll
+  for (int u = 0; u < MU * MU / 64; ++u) {
+    const int idx = lane + 64 * u, k = idx >> 4, c = idx & 15;
+    ub.ubd[u] = buf_load<T>(rd, (uint32_t)(k * n + c));
+  }
+}
+// parts: bit 0 W, bit 1 the pushed feedback
+template <typename T>
+__device__ inline void tile_loads(const SweepArgs<T>& a, int K, int w, int j, int parts,
+                                  TileLoads<T>& ld) {
+  const int64_t m = a.m, n = a.n;
+  const int lane = threadIdx.x & 63;
+  const int kq = lane >> 4, cl = lane & 15;
+  const int64_t r0 = (int64_t)K * BB;
+  const int mr = (m - r0) < BB ? (int)(m - r0) : BB;
+  const int64_t c0 = (int64_t)j * MU;
+  const int nc = (n - c0) < MU ? (int)(n - c0) : MU;
+  const int L = j / GOUT;
+  const int clo = GOUT * (L > 0 ? L - 1 : 0);
+  const int nwin = j - clo;
+  const int64_t es = sizeof(T);
+  const int64_t row0 = r0 + MU * w;
+  const int rows = mr - MU * w;  // (<= 0 for a wave without rows: nothing is read)
+  const int64_t tile_bytes = rows > 0 ? ((int64_t)(rows - 1) * n + nc) * es : 0;
+  const int64_t o0 = rows > 0 ? row0 * n + c0 : 0;
+  if (parts & 1) {
+    const rsrc_t rw = make_rsrc(a.W + o0, tile_bytes);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ld.win[e] = buf_load<T>(rw, (uint32_t)(Mfma<T>::row(lane, e) * n + cl));
+  }
+  if (parts & 2) {
+#pragma unroll
+    for (int c = 0; c < NCLS; ++c) {
+      const rsrc_t rvf =
+          make_rsrc(a.Vacc[c] + o0, expected_class(K, c) > 0 ? tile_bytes : 0);
+      const rsrc_t rhf =
+          make_rsrc(a.Hacc[c] + o0, expected_class(L, c) > 0 ? tile_bytes : 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t o = (uint32_t)(Mfma<T>::row(lane, e) * n + cl);
+        ld.vf[c][e] = buf_load_dev<T>(rvf, o);
+        ld.hf[c][e] = buf_load_dev<T>(rhf, o);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCLS; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ld.vf[c][e] = ld.hf[c][e] = T(0);
+  }
+}
+
+// At the end of phase p (p = -1: before the first), wave w issues the loads of its
+// micro-tile of phase p + 1, j = p + 1 - w (clamped into the band: ld is rewritten in
+// full every phase, so that it is dead between its use and the next phase).  The pushed
+// feedback is final once wave 0 has found the block's counters complete: wave 0 itself
+// checked them unless the tile starts a block; a later wave needs that check in an
+// earlier phase.  Returns whether the pushed feedback was loaded.
+template <typename T>
+__device__ inline bool prefetch_tile(const SweepArgs<T>& a, int K, int w, int p,
+                                     TileLoads<T>& ld) {
+  const int jn = p + 1 - w;
+  const int jc = jn < 0 ? 0 : (jn >= a.Nj ? a.Nj - 1 : jn);
+  const bool pushed = jn >= 0 && jn < a.Nj &&
+                      (w == 0 ? jn % GOUT != 0 : GOUT * (jn / GOUT) < p);
+  tile_loads<T>(a, K, w, jc, pushed ? 3 : 1, ld);
+  return pushed;
+}
+
+// Rounds micro-tile (w, j) of band K and stores its R, Delta, codes and Q.  Its input
+// loads were issued in the phase before (ld), and its pushed feedback too when `pre`.
+// Only wave 0 polls the progress and
+// contribution counters: a later wave reaches a micro-column or block at least one phase
+// (a barrier) after wave 0 found it ready, and skipping the polls keeps their waits, which
+// also wait for every load issued before them, off the other waves.
 template <typename T>
 __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, int K, int w,
-                                        int j, int& vblk, const T (&aVn)[BB / 4],
-                                        const T (&aVi)[3 * MU / 4], const T (&cu)[4], T cup,
-                                        T cup2, T s_r, T rs_r) {
+                                        int j, int& vblk, bool pre, TileLoads<T>& ld,
+                                        const T (&aVn)[BB / 4], const T (&aVi)[3 * MU / 4],
+                                        const T (&cu)[4], T cup, T cup2, T s_r, T rs_r) {
   typedef typename Mfma<T>::acc_t acc_t;
   constexpr int PR = BandSmem<T>::PR, PD = BandSmem<T>::PD;
   const int64_t m = a.m, n = a.n;
@@ -425,65 +534,45 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
 
   // Loads are issued in the order they are consumed (the counter that tracks them
   // retires in order): the U'b window and diagonal block and W first; then, once this
-  // 64-wide block's contribution counters are complete (checked once per block by each
-  // wave), the pushed feedback of both classes; last the R of the band above, whose product is
+  // 64-wide block's contribution counters are complete (checked once per block by wave
+  // 0), the pushed feedback of both classes; last the R of the band above, whose product is
   // computed after the others so that its latency overlaps them.
   const int64_t row0 = r0 + MU * w;  // first row of this micro-tile
   const int rows = mr - MU * w;      // valid rows (1..16)
   const int64_t tile_bytes = ((int64_t)(rows - 1) * n + nc) * es;
   const int64_t o0 = row0 * n + c0;
-  // U'b rows of the local window, this micro-column's columns (k-major B operand)
-  T bwin[7 * MU / 4];
-  {
-    const rsrc_t rb = make_rsrc(a.Ub + (int64_t)clo * MU * n + c0,
-                                nwin > 0 ? ((int64_t)(nwin * MU - 1) * n + nc) * es : 0);
+  UbLoads<T> ub;
+  ub_loads<T>(a, j, ub);
+  if (!pre) {
+    if (w == 0 && vblk != L) {
+      const int64_t tile = (int64_t)K * a.Nb + L;
 #pragma unroll
-    for (int s = 0; s < 7 * MU / 4; ++s)
-      bwin[s] = buf_load<T>(rb, (uint32_t)((4 * s + kq) * n + cl));
-  }
-  // diagonal micro-block of U'b (strictly upper part used)
-  T ubd[MU * MU / 64];
-  {
-    const rsrc_t rb = make_rsrc(a.Ub + c0 * n + c0, ((int64_t)(nc - 1) * n + nc) * es);
-#pragma unroll
-    for (int u = 0; u < MU * MU / 64; ++u) {
-      const int idx = lane + 64 * u, k = idx >> 4, c = idx & 15;
-      ubd[u] = buf_load<T>(rb, (uint32_t)(k * n + c));
+      for (int c = 0; c < NCLS; ++c) {
+        const int evc = expected_class(K, c), ehc = expected_class(L, c);
+        if (evc > 0 && !wait_ge(a.vcnt[c] + tile, evc, a.ctl, a.info)) return;
+        if (ehc > 0 && !wait_ge(a.hcnt[c] + tile, ehc, a.ctl, a.info)) return;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      vblk = L;
     }
+    tile_loads<T>(a, K, w, j, 2, ld);
   }
   T gin[4], hin[4];
-  {
-    const rsrc_t rw = make_rsrc(a.W + o0, tile_bytes);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) gin[e] = buf_load<T>(rw, (uint32_t)(Mfma<T>::row(lane, e) * n + cl));
-  }
-  if (vblk != L) {
-    const int64_t tile = (int64_t)K * a.Nb + L;
-#pragma unroll
-    for (int c = 0; c < NCLS; ++c) {
-      const int evc = expected_class(K, c), ehc = expected_class(L, c);
-      if (evc > 0 && !wait_ge(a.vcnt[c] + tile, evc, a.ctl, a.info)) return;
-      if (ehc > 0 && !wait_ge(a.hcnt[c] + tile, ehc, a.ctl, a.info)) return;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    vblk = L;
+  for (int e = 0; e < 4; ++e) {
+    gin[e] = ld.win[e];
+    hin[e] = T(0);
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) hin[e] = T(0);
-#pragma unroll
-  for (int c = 0; c < NCLS; ++c) {
-    const rsrc_t rvf =
-        make_rsrc(a.Vacc[c] + o0, expected_class(K, c) > 0 ? tile_bytes : 0);
-    const rsrc_t rhf =
-        make_rsrc(a.Hacc[c] + o0, expected_class(L, c) > 0 ? tile_bytes : 0);
+  for (int c = 0; c < NCLS; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t o = (uint32_t)(Mfma<T>::row(lane, e) * n + cl);
-      gin[e] -= buf_load_dev<T>(rvf, o);
-      hin[e] += buf_load_dev<T>(rhf, o);
+      gin[e] -= ld.vf[c][e];
+      hin[e] += ld.hf[c][e];
     }
-  }
-  if (K > 0 && !wait_ge(a.rdone + K - 1, j + 1, a.ctl, a.info)) return;
+  const T(&bwin)[7 * MU / 4] = ub.bwin;
+  const T(&ubd)[MU * MU / 64] = ub.ubd;
+  if (w == 0 && K > 0 && !wait_ge(a.rdone + K - 1, j + 1, a.ctl, a.info)) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   // R of the band above (k-major B operand).  When that band lives on this XCD its stores
   // went through this L2, so the shared L2 serves it; otherwise it is read at device scope.
@@ -781,7 +870,9 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
     }
 
     const int nphase = a.Nj + nw - 1;
-    int vblk = -1;  // last 64-wide block whose contribution counters this wave checked
+    int vblk = -1;  // last 64-wide block whose contribution counters wave 0 checked
+    TileLoads<T> ld;
+    bool pre = prefetch_tile<T>(a, K, w, -1, ld);  // ld: this phase's micro-tile loads
     for (int p = 0; p < nphase; ++p) {
       const int cdone = p - (nw - 1);  // micro-column completed by this phase
       const bool closes = cdone >= 0 && ((cdone & 3) == 3 || cdone == a.Nj - 1);
@@ -797,8 +888,10 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
       const int j = p - w;
       // (after an abort every wait inside returns at once, so the band drains quickly)
       if (w < nw && j >= 0 && j < a.Nj)
-        round_micro_tile<T>(a, sm, K, w, j, vblk, aVn, aVi, cu, cup, cup2, s_r, rs_r);
+        round_micro_tile<T>(a, sm, K, w, j, vblk, pre, ld, aVn, aVi, cu, cup, cup2, s_r, rs_r);
       drain();
+      // the next micro-tile's loads, in flight across the barrier
+      pre = prefetch_tile<T>(a, K, w, p, ld);
       __syncthreads();
       if (pub && cdone >= 0) {
         if (closes) publish_block(a, K, cdone / GOUT, base, lane);
