@@ -532,19 +532,20 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
   const int s4 = j & 3, s8 = j & 7;
   const int64_t es = sizeof(T);
 
-  // Loads are issued in the order they are consumed (the counter that tracks them
-  // retires in order): the U'b window and diagonal block and W first; then, once this
-  // 64-wide block's contribution counters are complete (checked once per block by wave
-  // 0), the pushed feedback of both classes; last the R of the band above, whose product is
+  // W and (inside a block) the pushed feedback were loaded in the phase before.  This
+  // phase's loads are issued in the order they are consumed (the counter that tracks them
+  // retires in order): the U'b window and diagonal block first; then, at a block's first
+  // micro-tile, the pushed feedback of every class (once wave 0 has found the block's
+  // contribution counters complete); last the R of the band above, whose product is
   // computed after the others so that its latency overlaps them.
   const int64_t row0 = r0 + MU * w;  // first row of this micro-tile
   const int rows = mr - MU * w;      // valid rows (1..16)
   const int64_t tile_bytes = ((int64_t)(rows - 1) * n + nc) * es;
   const int64_t o0 = row0 * n + c0;
-  UbLoads<T> ub;
-  ub_loads<T>(a, j, ub);
-  if (!pre) {
-    if (w == 0 && vblk != L) {
+  // wave 0's polls come before this phase's loads, so that they only wait for the loads
+  // issued in the phase before
+  if (w == 0) {
+    if (!pre && vblk != L) {
       const int64_t tile = (int64_t)K * a.Nb + L;
 #pragma unroll
       for (int c = 0; c < NCLS; ++c) {
@@ -552,11 +553,14 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
         if (evc > 0 && !wait_ge(a.vcnt[c] + tile, evc, a.ctl, a.info)) return;
         if (ehc > 0 && !wait_ge(a.hcnt[c] + tile, ehc, a.ctl, a.info)) return;
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       vblk = L;
     }
-    tile_loads<T>(a, K, w, j, 2, ld);
+    if (K > 0 && !wait_ge(a.rdone + K - 1, j + 1, a.ctl, a.info)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
+  UbLoads<T> ub;
+  ub_loads<T>(a, j, ub);
+  if (!pre) tile_loads<T>(a, K, w, j, 2, ld);
   T gin[4], hin[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -572,8 +576,6 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
     }
   const T(&bwin)[7 * MU / 4] = ub.bwin;
   const T(&ubd)[MU * MU / 64] = ub.ubd;
-  if (w == 0 && K > 0 && !wait_ge(a.rdone + K - 1, j + 1, a.ctl, a.info)) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   // R of the band above (k-major B operand).  When that band lives on this XCD its stores
   // went through this L2, so the shared L2 serves it; otherwise it is read at device scope.
   // Only in fp64: there a micro-tile row is one whole 128-byte line (n a multiple of 16
@@ -890,13 +892,15 @@ __device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
       if (w < nw && j >= 0 && j < a.Nj)
         round_micro_tile<T>(a, sm, K, w, j, vblk, pre, ld, aVn, aVi, cu, cup, cup2, s_r, rs_r);
       drain();
+      // Micro-column cdone is complete once the trailing wave's stores have drained (the
+      // other waves' tiles of it were drained before earlier barriers): the next band is
+      // told at once, not after this phase's barrier, which waits for this band's other
+      // waves.
+      if (pub && cdone >= 0 && lane == 0) st_dev(a.rdone + K, cdone + 1);
       // the next micro-tile's loads, in flight across the barrier
       pre = prefetch_tile<T>(a, K, w, p, ld);
       __syncthreads();
-      if (pub && cdone >= 0) {
-        if (closes) publish_block(a, K, cdone / GOUT, base, lane);
-        if (lane == 0) st_dev(a.rdone + K, cdone + 1);
-      }
+      if (pub && closes) publish_block(a, K, cdone / GOUT, base, lane);
     }
   }
 }
