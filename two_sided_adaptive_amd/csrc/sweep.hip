@@ -811,7 +811,9 @@ __device__ inline void publish_block(const SweepArgs<T>& a, int K, int L, int ba
 }
 
 template <typename T>
-__device__ void band_worker(const SweepArgs<T>& a, BandSmem<T>& sm) {
+// (inlined into the kernel: as a call it would take the kernel arguments through memory)
+__device__ __attribute__((always_inline)) inline void band_worker(const SweepArgs<T>& a,
+                                                                  BandSmem<T>& sm) {
   const int64_t m = a.m;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1076,7 +1078,9 @@ __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t l
 }
 
 template <typename T>
-__device__ void gemm_worker(const SweepArgs<T>& a, GemmSmem<T>& sm, int cls) {
+// (inlined into the kernel: as a call it would take the kernel arguments through memory)
+__device__ __attribute__((always_inline)) inline void gemm_worker(const SweepArgs<T>& a,
+                                                                  GemmSmem<T>& sm, int cls) {
   const int64_t m = a.m, n = a.n;
   const int tid = threadIdx.x;
   for (;;) {
