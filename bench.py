@@ -236,6 +236,26 @@ def main():
         adt_s = (time.perf_counter() - t0) / args.steps
         alt = {"dtype": adt, "ms_per_step": adt_s * 1e3, "value": m * n / adt_s,
                "codes_equal_to_headline": float((acodes == codes).float().mean().item())}
+        # the same steps with the event hook on: the sweep kernel and the band-update tasks
+        # of this dtype against its own MFMA peak
+        g2d.profile_enable(True)
+        g2d.profile_read()
+        for _ in range(args.steps):
+            g2d.quantize(aW, aA, aB, wl.bits, a_s, check=False, workspace=aws, out=(acodes, aQ))
+        torch.cuda.synchronize()
+        aprof = g2d.profile_read()
+        g2d.profile_enable(False)
+        apeak = PEAK["fp32_tflops"] if adt == "f32" else PEAK["fp64_tflops"]
+        sw = aprof.get("sweep")
+        if sw is not None and sw[1] > 0 and sw[0] > 0:
+            alt["sweep_ms_per_launch"] = sw[0] / sw[1]
+            alt["sweep_tflops"] = sw[2] / (sw[0] / 1e3) / 1e12
+        bg = aprof.get("band_gemm")
+        if bg is not None and bg[1] > 0 and bg[0] > 0:
+            rate = bg[2] / (bg[0] / 1e3) / 1e12 * ncu
+            alt["band_gemm"] = {"achieved": rate, "peak": apeak, "frac": rate / apeak,
+                                "unit": "TFLOP/s (per busy CU x CUs)",
+                                "tasks_per_step": bg[1] / args.steps}
         log(f"[bench] {adt} sweep: {adt_s * 1e3:.2f} ms/step")
         del aW, aA, aB, a_s, acodes, aQ, aws
     cpu = None
