@@ -61,7 +61,7 @@ def test_odd_shapes_fp64_exact(g2d, shape):
     np.testing.assert_array_equal(Q, ref["Q"])
 
 
-@pytest.mark.parametrize("p", [1, 5, 64, 65, 200, 512])
+@pytest.mark.parametrize("p", [1, 5, 64, 65, 200, 512, 1100])
 def test_factor_matches_oracle(g2d, p):
     wl = make_random(p, 2, 4, seed=p)
     for dtype, tol in (("f64", 1e-10), ("f32", 1e-5)):
@@ -71,6 +71,17 @@ def test_factor_matches_oracle(g2d, p):
         err = np.max(np.abs(U - ref)) / max(1.0, np.max(np.abs(ref)))
         assert err < tol, (dtype, err)
         assert np.all(np.tril(U, -1) == 0)
+
+
+def test_pair_with_long_inverse_rows_fp64_exact(g2d):
+    # 10 and 17 row tiles of 64: the factors' inverse rows take up to three chunks, and the
+    # two matrices' task groups interleave with different lengths
+    m, n = 600, 1030
+    wl = make_random(m, n, 3, seed=606)
+    (W, A, B, s), z, Q = _run(g2d, wl, "f64")
+    ref = oracle.quantize(W, A, B, s, 3)
+    assert np.array_equal(z, ref["Z"]), f"{int(np.sum(z != ref['Z']))} mismatches"
+    np.testing.assert_array_equal(Q, ref["Q"])
 
 
 def test_c2_fp64_exact(g2d):
