@@ -33,7 +33,7 @@
  *     DEVICE int[2] that the call first clears (may be NULL): info[0] = 1 if A is
  *     not positive definite, 2 if B is not, 3 if a scale is <= 0 or not finite,
  *     4 if a dependency wait inside one of the persistent kernels (the sweep, or the
- *     Cholesky of the factor stage) exceeded its bound (the kernel then stops early
+ *     factor stage's Cholesky and inverse) exceeded its bound (the kernel then stops early
  *     instead of hanging; this only happens when the device cannot keep the kernel's
  *     workgroups resident); info[1] = 1-based index
  *     of the failing pivot or row.  When info[0] != 0 the outputs are undefined.

@@ -13,7 +13,7 @@ enum KernelClass : int {
   KC_BAND_GEMM = 1,  // band-update tasks inside the sweep (busy time of the workgroups
                      // that ran them, in CU-milliseconds; one "launch" per task)
   KC_FACTOR = 2,     // the persistent Cholesky + inverse kernel of the factor stage
-  KC_OTHER = 3,      // reverse/finalize/init/check kernels
+  KC_OTHER = 3,      // setup, init and check kernels
   KC_COUNT = 4
 };
 
