@@ -16,6 +16,11 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
                          lattices (bits=16, no clamp: Babai's error bound)
   certificate            pinned: detects planted code flips
   objective              pinned: explicit Kronecker quadratic form
+  quantize3 (three       pinned: quartic vectorised GPTQ with the explicit
+    Kronecker factors)   three-factor Gram, reduction to the two-factor sweep
+                         (m3 = 1 and m1 = 1), independent slabs (A1 = I),
+                         three-mode certificate, mode-permutation symmetry
+  objective3             pinned: explicit Kronecker quadratic form
 """
 from .gptq2d import (  # noqa: F401
     babai_nearest_plane,
@@ -29,4 +34,11 @@ from .gptq2d import (  # noqa: F401
     quantize,
     rtn,
     sweep,
+)
+from .kron3 import (  # noqa: F401
+    certificate3,
+    gptq_vectorized3,
+    objective3,
+    quantize3,
+    quantize3_factored,
 )

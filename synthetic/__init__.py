@@ -5,4 +5,5 @@ per-row grid scales).  It holds none of the rounding method's arithmetic, so the
 CPU oracle and the GPU library can both consume its arrays without sharing any
 code of the method itself.
 """
-from .configs import CONFIG_NAMES, Workload, make, make_random  # noqa: F401
+from .configs import (  # noqa: F401
+    CONFIG_NAMES, SHAPES3, Workload, Workload3, make, make3, make_random, make_random3)

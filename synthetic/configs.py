@@ -259,3 +259,74 @@ def make_random(m: int, n: int, bits: int = 4, seed: int = 0, dtype: str = "f64"
     if global_scale:
         wl.scales[:] = _round_through(np.array([np.max(np.abs(wl.W)) / wl.hi]), dtype)[0]
     return wl
+
+
+# --------------------------------------------------------------------------
+# three-factor (tensor) workloads
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Workload3:
+    """A 3-way weight tensor W (m1 x m2 x m3) under the Gram A1 (x) A2 (x) A3.
+
+    scales has shape (m1, m2): one grid step per fibre along the last mode (for
+    m1 = 1 this is the per-row scale of the two-factor problem).
+    """
+    name: str
+    W: np.ndarray
+    A1: np.ndarray
+    A2: np.ndarray
+    A3: np.ndarray
+    scales: np.ndarray
+    bits: int
+    dtype: str
+    recipe: str
+
+    @property
+    def shape(self):
+        return self.W.shape
+
+
+def _finish3(name, w, a1, a2, a3, bits, dtype, recipe) -> Workload3:
+    w = _round_through(w, dtype)
+    hi = (1 << (bits - 1)) - 1
+    s = _round_through(np.max(np.abs(w), axis=2) / float(hi), dtype)
+    mats = [np.ascontiguousarray(_round_through(_sym(a), dtype)) for a in (a1, a2, a3)]
+    return Workload3(name, np.ascontiguousarray(w), *mats, np.ascontiguousarray(s), bits,
+                     dtype, recipe)
+
+
+SHAPES3 = {"K1": (4, 96, 80, 4), "K2": (16, 1024, 1024, 4)}
+
+
+def make3(name: str) -> Workload3:
+    """Three-factor workloads: K1 a small parity case, K2 the measured size.
+
+    K2 stands for a stack of 16 square 1024-wide blocks (heads or experts) whose
+    Hessian factors over stack index, rows and columns; each factor is a Wishart
+    matrix of AR(1) samples as in the 4096-wide layer, the stack factor with a
+    stronger correlation (rho = 0.5) so that the mode-1 feedback matters.
+    """
+    if name not in SHAPES3:
+        raise KeyError(f"unknown workload {name!r}; known: {tuple(SHAPES3)}")
+    m1, m2, m3, bits = SHAPES3[name]
+    gw, g1, g2, g3 = _streams(707 if name == "K1" else 808)
+    w = 0.015 * gw.standard_normal((m1, m2, m3))
+    a1 = _wishart_ar1(g1, m1, 4 * m1, 0.5)
+    a2 = _wishart_ar1(g2, m2, 2 * m2, 0.3)
+    a3 = _wishart_ar1(g3, m3, 2 * m3, 0.3)
+    return _finish3(name, w, a1, a2, a3, bits, "f64",
+                    f"{m1}x{m2}x{m3} fp64; W~N(0,0.015^2); A1 Wishart of {4 * m1} AR(1) "
+                    f"samples rho=0.5, A2/A3 of 2p samples rho=0.3, + 1% damping; {bits}-bit")
+
+
+def make_random3(m1: int, m2: int, m3: int, bits: int = 4, seed: int = 0,
+                 dtype: str = "f64", kind: str = "wishart") -> Workload3:
+    """Small random tensor problem; kind "identity1" makes A1 the identity."""
+    gw, g1, g2, g3 = _streams(20_000 + seed)
+    w = 0.02 * gw.standard_normal((m1, m2, m3))
+    a1 = np.eye(m1) if kind == "identity1" else _wishart_iid(g1, m1, max(m1, 8), 0.05)
+    a2 = _wishart_iid(g2, m2, max(m2, 8), 0.05)
+    a3 = _wishart_iid(g3, m3, max(m3, 8), 0.05)
+    return _finish3(f"rand3_{m1}x{m2}x{m3}b{bits}s{seed}{kind}", w, a1, a2, a3, bits, dtype,
+                    f"random3 {kind}")
