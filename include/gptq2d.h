@@ -111,9 +111,34 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
 size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype);
 
 /*
+ * Three Kronecker factors ("GPTQ-2D: Cubic-Time Two-Sided Adaptive Rounding", arxivlens
+ * page, Abstract: the algorithm extends to Hessians with any number of Kronecker
+ * factors).  W is an m1 x m2 x m3 tensor (row-major: the last index is fastest) and the
+ * Gram of its vectorisation is A1 (x) A2 (x) A3; the result is the trajectory of
+ * one-dimensional GPTQ on that vectorisation, in that order.  Rounded slab by slab:
+ * slab k (the m2 x m3 matrix W[k]) receives the feedback of the earlier slabs through
+ * U1', then is rounded as a two-factor problem under (A2, A3) by the sweep.
+ *   m1, m2, m3  tensor extents, each in [1, 262140]                   [args 1-3]
+ *   bits, dtype                                                        [args 4-5]
+ *   W        m1 x m2 x m3                                               [arg 6]
+ *   A1, A2, A3  m1 x m1, m2 x m2, m3 x m3 SPD (lower triangles read)  [args 7-9]
+ *   scales   m1 x m2: one grid step per fibre W[k][i][:]               [arg 10]
+ *   codes    m1 x m2 x m3 int8 out; Q m1 x m2 x m3 out (dtype)       [args 11-12]
+ *   workspace, workspace_bytes (gptq2d_workspace3_bytes), info, stream [args 13-16]
+ * info[0] = 5, 6 or 7 if A1, A2 or A3 is not positive definite; 3 for a bad scale, with
+ * info[1] the 1-based index of the row within its slab; 4 as above.
+ */
+int gptq2d_quantize3(int64_t m1, int64_t m2, int64_t m3, int bits, int dtype, const void* W,
+                     const void* A1, const void* A2, const void* A3, const void* scales,
+                     int8_t* codes, void* Q, void* workspace, size_t workspace_bytes, int* info,
+                     void* stream);
+size_t gptq2d_workspace3_bytes(int64_t m1, int64_t m2, int64_t m3, int dtype);
+
+/*
  * Measurement hook (not part of the method): when enabled, every kernel launch of
  * the library is bracketed by a pair of HIP events on its stream and accounted to a
- * kernel class (0 sweep, 2 factor: the persistent Cholesky and inverse, 3 other) with the
+ * kernel class (0 sweep, 2 factor: the persistent Cholesky and inverse, 3 other, 4 the
+ * mode-1 feedback between slabs of gptq2d_quantize3) with the
  * algorithmic flops and HBM bytes of that launch.  Class 1 (band_gemm) is counted
  * inside the persistent sweep kernel: its milliseconds are the summed busy time of the
  * workgroups that ran band-update tasks (CU-milliseconds), its launches the tasks and
@@ -121,7 +146,7 @@ size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype);
  * records to the stream and three atomics per band-update task while on.
  * gptq2d_profile_read waits for the recorded events, writes per-class totals since
  * the previous read (milliseconds, launches, flops, bytes; host arrays, any pointer
- * may be NULL) for the first min(n_classes, 4) classes and resets the totals.
+ * may be NULL) for the first min(n_classes, 5) classes and resets the totals.
  * Returns 0, -1 if n_classes < 0, or GPTQ2D_ERR_HIP if an event query failed.
  */
 int gptq2d_profile_enable(int on);

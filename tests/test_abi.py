@@ -75,3 +75,27 @@ def test_strerror(lib):
     assert lib.gptq2d_strerror(0) == b"success"
     assert b"argument" in lib.gptq2d_strerror(-3)
     assert lib.gptq2d_strerror(12345)
+
+
+def test_three_factor_arguments_rejected_on_host(lib):
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    q = lib.gptq2d_quantize3
+    ok = [4, 5, 6, 4, 1, p, p, p, p, p, p, p, None, 0, None, None]
+    assert q(*ok[:0], 0, *ok[1:]) == -1
+    for i, bad in [(1, 0), (2, -1), (3, 1), (3, 9), (4, 3)]:
+        args = list(ok)
+        args[i] = bad
+        assert q(*args) == -(i + 1), (i, bad)
+    for i in range(5, 12):  # null W, A1, A2, A3, scales, codes, Q
+        args = list(ok)
+        args[i] = None
+        assert q(*args) == -(i + 1), i
+    args = list(ok)
+    args[12], args[13] = p, 8
+    assert q(*args) == -14
+    args[12] = None
+    assert q(*args) == -14
+    assert lib.gptq2d_workspace3_bytes(0, 4, 4, 1) == 0
+    assert lib.gptq2d_workspace3_bytes(4, 4, 4, 3) == 0
+    w = lib.gptq2d_workspace3_bytes(16, 1024, 1024, 1)
+    assert w % 256 == 0 and w >= 16 * 1024 * 1024 * 8 + 2 * 1024 * 1024 * 8

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     profile_enable,
     profile_read,
     quantize,
+    quantize3,
     quantize_factored,
     workspace_bytes,
 )

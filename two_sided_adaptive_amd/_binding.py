@@ -32,6 +32,10 @@ _SYMBOLS = {
                                        ctypes.c_int] + [ctypes.c_void_p] * 6 +
                         [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "gptq2d_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
+    "gptq2d_quantize3": (ctypes.c_int, [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_int] +
+                         [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                  ctypes.c_void_p, ctypes.c_void_p]),
+    "gptq2d_workspace3_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 3 + [ctypes.c_int]),
     "gptq2d_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gptq2d_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "gptq2d_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -88,7 +92,9 @@ def _raise_rc(rc: int, fn: str) -> None:
 
 _INFO_MSG = {1: "A is not positive definite (pivot {})", 2: "B is not positive definite (pivot {})",
              3: "scale of row {} is not positive and finite",
-             4: "a dependency wait inside a persistent kernel timed out (outputs undefined)"}
+             4: "a dependency wait inside a persistent kernel timed out (outputs undefined)",
+             5: "A1 is not positive definite (pivot {})", 6: "A2 is not positive definite (pivot {})",
+             7: "A3 is not positive definite (pivot {})"}
 
 
 def _check_info(info: torch.Tensor) -> None:
@@ -171,6 +177,34 @@ def quantize(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, bits: int, scale
                              scales.data_ptr(), codes.data_ptr(), Q.data_ptr(), ws.data_ptr(),
                              ws.numel(), info.data_ptr(), _stream(W.device))
     _raise_rc(rc, "gptq2d_quantize")
+    if check:
+        _check_info(info)
+    return codes, Q
+
+
+def quantize3(W: torch.Tensor, A1: torch.Tensor, A2: torch.Tensor, A3: torch.Tensor, bits: int,
+              scales: torch.Tensor, check: bool = True, workspace: Optional[torch.Tensor] = None,
+              out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Three Kronecker factors (gptq2d_quantize3): W (m1, m2, m3), scales (m1, m2)."""
+    lib = load_library()
+    m1, m2, m3 = W.shape
+    dt = _dt(W)
+    _check_dev("W", W, W.dtype, (m1, m2, m3))
+    _check_dev("A1", A1, W.dtype, (m1, m1))
+    _check_dev("A2", A2, W.dtype, (m2, m2))
+    _check_dev("A3", A3, W.dtype, (m3, m3))
+    _check_dev("scales", scales, W.dtype, (m1, m2))
+    codes, Q = out if out is not None else (
+        torch.empty((m1, m2, m3), dtype=torch.int8, device=W.device), torch.empty_like(W))
+    need = lib.gptq2d_workspace3_bytes(m1, m2, m3, dt)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8,
+                                                             device=W.device)
+    info = torch.zeros(2, dtype=torch.int32, device=W.device)
+    rc = lib.gptq2d_quantize3(m1, m2, m3, int(bits), dt, W.data_ptr(), A1.data_ptr(),
+                              A2.data_ptr(), A3.data_ptr(), scales.data_ptr(), codes.data_ptr(),
+                              Q.data_ptr(), ws.data_ptr(), ws.numel(), info.data_ptr(),
+                              _stream(W.device))
+    _raise_rc(rc, "gptq2d_quantize3")
     if check:
         _check_info(info)
     return codes, Q

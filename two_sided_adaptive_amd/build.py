@@ -10,8 +10,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["api.hip", "factor.hip", "sweep.hip"]
-HEADERS = ["common.hpp", "launch.hpp"]
+SOURCES = ["api.hip", "factor.hip", "sweep.hip", "kron3.hip"]
+HEADERS = ["common.hpp", "launch.hpp", "prof.hpp"]
 LIB = os.path.join(PKG, "libgptq2d.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

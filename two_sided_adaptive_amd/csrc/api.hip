@@ -223,6 +223,41 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
   return status(e);
 }
 
+size_t gptq2d_workspace3_bytes(int64_t m1, int64_t m2, int64_t m3, int dtype) {
+  if (m1 <= 0 || m2 <= 0 || m3 <= 0 || m1 > kMaxDim || m2 > kMaxDim || m3 > kMaxDim ||
+      bad_dtype(dtype))
+    return 0;
+  return g2d::kron3_workspace(m1, m2, m3, dtype);
+}
+
+int gptq2d_quantize3(int64_t m1, int64_t m2, int64_t m3, int bits, int dtype, const void* W,
+                     const void* A1, const void* A2, const void* A3, const void* scales,
+                     int8_t* codes, void* Q, void* workspace, size_t workspace_bytes, int* info,
+                     void* stream) {
+  if (m1 <= 0 || m1 > kMaxDim) return -1;
+  if (m2 <= 0 || m2 > kMaxDim) return -2;
+  if (m3 <= 0 || m3 > kMaxDim) return -3;
+  if (bits < 2 || bits > 8) return -4;
+  if (bad_dtype(dtype)) return -5;
+  if (W == nullptr) return -6;
+  if (A1 == nullptr) return -7;
+  if (A2 == nullptr) return -8;
+  if (A3 == nullptr) return -9;
+  if (scales == nullptr) return -10;
+  if (codes == nullptr) return -11;
+  if (Q == nullptr) return -12;
+  const size_t need = gptq2d_workspace3_bytes(m1, m2, m3, dtype);
+  if (workspace != nullptr && workspace_bytes < need) return -14;
+  if (workspace == nullptr && workspace_bytes != 0) return -14;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch ws;
+  int rc = ws.acquire(workspace, workspace_bytes, need, s);
+  if (rc) return rc;
+  if ((rc = clear_info(info, s))) return rc;
+  return status(g2d::kron3_enqueue(m1, m2, m3, bits, dtype, W, A1, A2, A3, scales, codes, Q,
+                                   ws.ptr, info, s));
+}
+
 int gptq2d_profile_enable(int on) {
   g2d::ProfState& p = g2d::prof();
   std::lock_guard<std::mutex> g(p.mu);
@@ -271,7 +306,8 @@ int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* fl
 }
 
 const char* gptq2d_profile_class_name(int cls) {
-  static const char* names[g2d::KC_COUNT] = {"sweep", "band_gemm", "factor", "other"};
+  static const char* names[g2d::KC_COUNT] = {"sweep", "band_gemm", "factor", "other",
+                                                  "slab_feedback"};
   return (cls >= 0 && cls < g2d::KC_COUNT) ? names[cls] : "unknown";
 }
 

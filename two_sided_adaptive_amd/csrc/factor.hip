@@ -1077,9 +1077,9 @@ hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws
 
 hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, int64_t n,
                                const void* B, void* Ub, void* ws_b, int dtype, int* info,
-                               hipStream_t s) {
-  const FactorPlan qa = plan(m, dtype, A, Ua, ws_a, 1);
-  const FactorPlan qb = plan(n, dtype, B, Ub, ws_b, 2);
+                               hipStream_t s, int code_a, int code_b) {
+  const FactorPlan qa = plan(m, dtype, A, Ua, ws_a, code_a);
+  const FactorPlan qb = plan(n, dtype, B, Ub, ws_b, code_b);
   const FactorPlan* qs[2] = {&qa, &qb};
   return chol_persistent_enqueue(qs, 2, 2, info, s);
 }

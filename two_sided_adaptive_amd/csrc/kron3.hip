@@ -1,0 +1,145 @@
+// Three Kronecker factors ("GPTQ-2D: Cubic-Time Two-Sided Adaptive Rounding", arxivlens
+// page, Abstract: the method extends to Hessians with any number of Kronecker factors).
+//
+// W is an m1 x m2 x m3 tensor under A1 (x) A2 (x) A3.  The unit feedback factor of the
+// Kronecker Gram is U1' (x) U2' (x) U3', so the rounding splits into slabs W[k] (m2 x m3):
+// slab k's target is W[k] - sum_{j<k} U1'[j,k] R1[j], where R1[j] = (slab j's target) -
+// Q[j], and each target is then rounded as a two-factor problem (A2, A3) by the sweep
+// kernel.  The mode-1 feedback is lazy in blocks of kSlabBlock slabs, as GPTQ's own
+// blocking: a slab pulls the terms of the earlier slabs of its block just before its
+// sweep, and a finished block pushes its terms to every later slab in one pass.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "prof.hpp"
+
+namespace g2d {
+namespace {
+
+constexpr int kSlabBlock = 16;
+
+// Wg[r] -= U1[j, r] * (Wg[j] - Q[j]) for every row r in [r0, r1) and j = j0 .. j1-1
+// (j1 - j0 <= kSlabBlock, all j < r0), one thread per slab entry.  The terms are applied
+// one by one in ascending j, each as a rounded product then a rounded subtraction (no
+// fused multiply-add), so every entry sees exactly the sequence of operations of the
+// plain one-axpy-per-slab definition whatever the blocking.
+template <typename T>
+__global__ __launch_bounds__(256) void k_slab_feedback(T* __restrict__ Wg,
+                                                       const T* __restrict__ Q,
+                                                       const T* __restrict__ U1, int64_t m1,
+                                                       int64_t slab, int r0, int r1, int j0,
+                                                       int j1) {
+#pragma clang fp contract(off)
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= slab) return;
+  const int nj = j1 - j0;
+  T res[kSlabBlock];
+#pragma unroll
+  for (int t = 0; t < kSlabBlock; ++t)
+    res[t] = t < nj ? Wg[(int64_t)(j0 + t) * slab + c] - Q[(int64_t)(j0 + t) * slab + c] : T(0);
+  for (int r = r0 + (int)blockIdx.y; r < r1; r += (int)gridDim.y) {
+    T g = Wg[(int64_t)r * slab + c];
+#pragma unroll
+    for (int t = 0; t < kSlabBlock; ++t) {
+      if (t < nj) {
+        const T prod = U1[(int64_t)(j0 + t) * m1 + r] * res[t];
+        g = g - prod;
+      }
+    }
+    Wg[(int64_t)r * slab + c] = g;
+  }
+}
+
+template <typename T>
+hipError_t slab_feedback(T* Wg, const T* Q, const T* U1, int64_t m1, int64_t slab, int r0,
+                         int r1, int j0, int j1, hipStream_t s) {
+  if (r1 <= r0 || j1 <= j0) return hipSuccess;
+  if (j1 - j0 > kSlabBlock || j1 > r0) return hipErrorInvalidValue;
+  const int64_t gx = cdiv(slab, 256);
+  if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  int64_t gy = cdiv(2048, gx);  // enough workgroups for small slabs
+  if (gy > r1 - r0) gy = r1 - r0;
+  if (gy > 65535) gy = 65535;
+  const double es = (double)sizeof(T);
+  prof_begin(KC_SLAB, s);
+  k_slab_feedback<T><<<dim3((unsigned)gx, (unsigned)gy), 256, 0, s>>>(Wg, Q, U1, m1, slab, r0,
+                                                                       r1, j0, j1);
+  prof_end(KC_SLAB, s, 2.0 * (double)(j1 - j0) * (double)(r1 - r0) * (double)slab,
+           es * (double)slab * (2.0 * (double)(j1 - j0) * (double)gy + 2.0 * (double)(r1 - r0)));
+  return hipGetLastError();
+}
+
+struct Kron3Ws {
+  void *U1, *U2, *U3, *Wg, *scratch, *scratch3;
+};
+
+Kron3Ws carve3(int64_t m1, int64_t m2, int64_t m3, int dtype, void* ws) {
+  const size_t es = dtype == 0 ? sizeof(float) : sizeof(double);
+  char* c = (char*)ws;
+  Kron3Ws w;
+  w.U1 = c;
+  c += align_up((size_t)m1 * m1 * es);
+  w.U2 = c;
+  c += align_up((size_t)m2 * m2 * es);
+  w.U3 = c;
+  c += align_up((size_t)m3 * m3 * es);
+  w.Wg = c;
+  c += align_up((size_t)m1 * m2 * m3 * es);
+  w.scratch = c;
+  w.scratch3 = c + factor_workspace(m2);
+  return w;
+}
+
+template <typename T>
+hipError_t kron3_typed(int64_t m1, int64_t m2, int64_t m3, int bits, int dtype, const T* W,
+                       const T* A1, const T* A2, const T* A3, const T* scales, int8_t* codes,
+                       T* Q, void* ws, int* info, hipStream_t s) {
+  const Kron3Ws w = carve3(m1, m2, m3, dtype, ws);
+  const int64_t slab = m2 * m3;
+  T* Wg = (T*)w.Wg;
+  const T* U1 = (const T*)w.U1;
+  hipError_t e = factor_pair_enqueue(m2, A2, w.U2, w.scratch, m3, A3, w.U3, w.scratch3, dtype,
+                                     info, s, kInfoA2, kInfoA3);
+  if (e == hipSuccess) e = factor_enqueue(m1, dtype, A1, w.U1, w.scratch, info, kInfoA1, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(Wg, W, (size_t)m1 * slab * sizeof(T), hipMemcpyDeviceToDevice, s);
+  for (int64_t b = 0; e == hipSuccess && b < m1; b += kSlabBlock) {
+    const int64_t end = b + kSlabBlock < m1 ? b + kSlabBlock : m1;
+    for (int64_t k = b; e == hipSuccess && k < end; ++k) {
+      e = slab_feedback<T>(Wg, Q, U1, m1, slab, (int)k, (int)k + 1, (int)b, (int)k, s);
+      if (e == hipSuccess)
+        e = sweep_enqueue(m2, m3, bits, dtype, Wg + k * slab, w.U2, w.U3, scales + k * m2,
+                          codes + k * slab, Q + k * slab, w.scratch, info, s);
+    }
+    if (e == hipSuccess)
+      e = slab_feedback<T>(Wg, Q, U1, m1, slab, (int)end, (int)m1, (int)b, (int)end, s);
+  }
+  return e;
+}
+
+}  // namespace
+
+size_t kron3_workspace(int64_t m1, int64_t m2, int64_t m3, int dtype) {
+  const size_t es = dtype == 0 ? sizeof(float) : sizeof(double);
+  size_t scratch = factor_workspace(m2) + factor_workspace(m3);
+  if (factor_workspace(m1) > scratch) scratch = factor_workspace(m1);
+  const size_t sw = sweep_workspace(m2, m3, dtype);
+  if (sw > scratch) scratch = sw;
+  return align_up((size_t)m1 * m1 * es) + align_up((size_t)m2 * m2 * es) +
+         align_up((size_t)m3 * m3 * es) + align_up((size_t)m1 * m2 * m3 * es) + scratch;
+}
+
+hipError_t kron3_enqueue(int64_t m1, int64_t m2, int64_t m3, int bits, int dtype, const void* W,
+                         const void* A1, const void* A2, const void* A3, const void* scales,
+                         int8_t* codes, void* Q, void* ws, int* info, hipStream_t s) {
+  if (dtype == 0)
+    return kron3_typed<float>(m1, m2, m3, bits, dtype, (const float*)W, (const float*)A1,
+                              (const float*)A2, (const float*)A3, (const float*)scales, codes,
+                              (float*)Q, ws, info, s);
+  return kron3_typed<double>(m1, m2, m3, bits, dtype, (const double*)W, (const double*)A1,
+                             (const double*)A2, (const double*)A3, (const double*)scales, codes,
+                             (double*)Q, ws, info, s);
+}
+
+}  // namespace g2d

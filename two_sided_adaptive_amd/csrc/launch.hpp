@@ -16,15 +16,24 @@ size_t factor_workspace(int64_t p);
 hipError_t factor_enqueue(int64_t p, int dtype, const void* A, void* U, void* ws, int* info,
                           int side_code, hipStream_t s);
 // Both factors at once, in one persistent launch on s: A (m x m) and B (n x n); info codes
-// 1 for A and 2 for B.
+// code_a for A and code_b for B.
 hipError_t factor_pair_enqueue(int64_t m, const void* A, void* Ua, void* ws_a, int64_t n,
                                const void* B, void* Ub, void* ws_b, int dtype, int* info,
-                               hipStream_t s);
+                               hipStream_t s, int code_a = 1, int code_b = 2);
+
+// info codes of the three-factor call: a non-SPD A1, A2 or A3.
+constexpr int kInfoA1 = 5, kInfoA2 = 6, kInfoA3 = 7;
 
 // Sweep stage (sweep.hip): codes/Q from W, U'_a, U'_b, scales (all dtype).
 size_t sweep_workspace(int64_t m, int64_t n, int dtype);
 hipError_t sweep_enqueue(int64_t m, int64_t n, int bits, int dtype, const void* W,
                          const void* Ua, const void* Ub, const void* scales, int8_t* codes,
                          void* Q, void* ws, int* info, hipStream_t s);
+
+// Three Kronecker factors (kron3.hip): codes/Q of an m1 x m2 x m3 tensor (all dtype).
+size_t kron3_workspace(int64_t m1, int64_t m2, int64_t m3, int dtype);
+hipError_t kron3_enqueue(int64_t m1, int64_t m2, int64_t m3, int bits, int dtype, const void* W,
+                         const void* A1, const void* A2, const void* A3, const void* scales,
+                         int8_t* codes, void* Q, void* ws, int* info, hipStream_t s);
 
 }  // namespace g2d

@@ -14,7 +14,8 @@ enum KernelClass : int {
                      // that ran them, in CU-milliseconds; one "launch" per task)
   KC_FACTOR = 2,     // the persistent Cholesky + inverse kernel of the factor stage
   KC_OTHER = 3,      // setup, init and check kernels
-  KC_COUNT = 4
+  KC_SLAB = 4,       // mode-1 feedback between the slabs of a three-factor tensor
+  KC_COUNT = 5
 };
 
 bool prof_on();
