@@ -106,6 +106,88 @@ def cpu_baseline(wl, W, A, B, s, z_gpu, rows):
     }
 
 
+def kron3_leg(steps, warmup, cpu, peak):
+    """Three Kronecker factors on the 16 x 1024 x 1024 tensor K2 (fp64): time per call,
+    per-class kernel figures, and the oracle on its first two slabs."""
+    import numpy as np
+    import torch
+
+    import two_sided_adaptive_amd as g2d
+    from synthetic import make3
+
+    wl = make3("K2")
+    m1, m2, m3 = wl.W.shape
+    dev = torch.device("cuda:0")
+    t = [torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+         for x in (wl.W, wl.A1, wl.A2, wl.A3, wl.scales)]
+    codes = torch.empty((m1, m2, m3), dtype=torch.int8, device=dev)
+    Q = torch.empty_like(t[0])
+    ws = torch.empty(g2d.load_library().gptq2d_workspace3_bytes(m1, m2, m3, 1),
+                     dtype=torch.uint8, device=dev)
+
+    def call(check=False):
+        g2d.quantize3(t[0], t[1], t[2], t[3], wl.bits, t[4], check=check, workspace=ws,
+                      out=(codes, Q))
+
+    for _ in range(warmup):
+        call()
+    call(check=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    g2d.profile_enable(True)
+    g2d.profile_read()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    prof = g2d.profile_read()
+    g2d.profile_enable(False)
+    kernels = {}
+    for name, (ms, launches, flops, byts) in prof.items():
+        if launches == 0 or name == "band_gemm":
+            continue
+        sec = ms / 1e3
+        kernels[name] = {"ms_per_call": ms / steps, "launches_per_call": launches / steps,
+                         "avg_launch_us": 1e3 * ms / launches,
+                         "tflops": flops / sec / 1e12 if sec > 0 else None,
+                         "gbs": byts / sec / 1e9 if sec > 0 else None}
+    out = {"workload": f"K2: {m1}x{m2}x{m3} {wl.bits}-bit tensor under A1 (x) A2 (x) A3, fp64",
+           "recipe": wl.recipe, "ms_per_call": dt * 1e3, "value": wl.W.size / dt,
+           "unit": "entries/s", "kernels": kernels}
+    sw, fb = kernels.get("sweep"), kernels.get("slab_feedback")
+    if sw and sw["tflops"]:
+        out["roofline_sweep"] = {"bound": "mfma", "achieved": sw["tflops"],
+                                 "peak": peak["fp64_tflops"], "unit": "TFLOP/s",
+                                 "frac": sw["tflops"] / peak["fp64_tflops"]}
+    if fb and fb["gbs"]:
+        out["roofline_slab_feedback"] = {"bound": "hbm", "achieved": fb["gbs"],
+                                         "peak": peak["hbm_gbs"], "unit": "GB/s",
+                                         "frac": fb["gbs"] / peak["hbm_gbs"]}
+    if cpu:
+        import oracle
+        oracle.build_library(force=False)
+        k = 2
+        t0 = time.perf_counter()
+        U1, U2, U3 = (oracle.factor_unit_upper(a) for a in (wl.A1, wl.A2, wl.A3))
+        t1 = time.perf_counter()
+        # the first k slabs are an exact sub-problem (slabs only feed later slabs), with the
+        # leading k x k block of the full U1'
+        ref = oracle.quantize3_factored(wl.W[:k], U1[:k, :k], U2, U3, wl.scales[:k], wl.bits)
+        t2 = time.perf_counter()
+        t_full = (t1 - t0) + (t2 - t1) * m1 / k
+        out["cpu_baseline"] = {
+            "value": wl.W.size / t_full, "unit": "entries/s", "kind": "oracle",
+            "sample": f"LAPACK factors of A1, A2, A3 in {t1 - t0:.2f} s + nested sweep of the "
+                      f"first {k} slabs in {t2 - t1:.2f} s, scaled by {m1 // k} to {m1} slabs: "
+                      f"est. {t_full:.1f} s/tensor",
+            "gpu_code_agreement_on_sample": float(
+                np.mean(ref["Z"] == codes[:k].cpu().numpy().astype(np.int32)))}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +200,10 @@ def main():
     ap.add_argument("--no-alt", action="store_true", help="skip timing the other sweep dtype")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kron3", action="store_true",
+                    help="skip the three-factor tensor leg (K2, 16x1024x1024)")
+    ap.add_argument("--kron3-only", action="store_true",
+                    help="run only the three-factor leg and print its JSON object")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -141,6 +227,10 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     g2d.load_library()
+    if args.kron3_only:
+        print(json.dumps(kron3_leg(args.steps, args.warmup, not args.no_cpu_baseline, PEAK)),
+              flush=True)
+        return
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
     wl = make(args.workload, cache_dir=os.environ.get("GPTQ2D_CACHE"))
@@ -263,6 +353,10 @@ def main():
         log(f"[bench] cpu baseline: oracle on the first {args.cpu_rows} rows")
         cpu = cpu_baseline(wl, W.astype(np.float64), A.astype(np.float64),
                            B.astype(np.float64), s.astype(np.float64), z_gpu, args.cpu_rows)
+    k3 = None
+    if not args.no_kron3:
+        log("[bench] three-factor leg (K2)")
+        k3 = kron3_leg(max(1, min(args.steps, 5)), 1, not args.no_cpu_baseline, PEAK)
     out = {
         "metric": METRIC, "value": m * n / dt, "unit": "entries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3,
@@ -277,6 +371,7 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
         "other_dtype": alt,
+        "kron3": k3,
     }
     print(json.dumps(out), flush=True)
 
