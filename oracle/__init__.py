@@ -21,6 +21,10 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
                          (m3 = 1 and m1 = 1), independent slabs (A1 = I),
                          three-mode certificate, mode-permutation symmetry
   objective3             pinned: explicit Kronecker quadratic form
+  packing.pack_rows /    pinned: hand-worked 3-bit row (tests/golden), byte and
+    unpack_rows          nibble views for 8 and 4 bits, round trip, zero padding
+  packing.dequantize /   pinned: equals the quantizer's Q; explicit dot products
+    packed_gemv
 """
 from .gptq2d import (  # noqa: F401
     babai_nearest_plane,
