@@ -135,10 +135,37 @@ int gptq2d_quantize3(int64_t m1, int64_t m2, int64_t m3, int bits, int dtype, co
 size_t gptq2d_workspace3_bytes(int64_t m1, int64_t m2, int64_t m3, int dtype);
 
 /*
+ * Packed codes: the step after the quantizer, whose output is an integer matrix
+ * ("GPTQ-2D: Cubic-Time Two-Sided Adaptive Rounding", arxivlens page, Abstract).  The pages
+ * define no storage format; this one is dense: a code z in [lo, hi] is the field
+ * u = z - lo (bits wide); row r is one little-endian bit string in which code c occupies
+ * bits c*bits .. c*bits+bits-1, held in gptq2d_packed_row_words(n, bits) = ceil(n*bits/32)
+ * uint32 words (row-major, rows back to back); padding bits are zero.  rows, n >= 1 and
+ * <= 2^40; bits in [2, 8].  Device pointers; enqueued on `stream`.
+ *
+ * gptq2d_pack: codes (rows x n int8, values in [lo, hi]; others are stored modulo 2^bits)
+ *   -> packed (rows x words uint32).                        args: rows, n, bits, codes, packed
+ * gptq2d_unpack: Q = s[r] * z (rows x n, dtype) from packed and scales (rows, dtype).
+ *   args: rows, n, bits, dtype, packed, scales, Q
+ * gptq2d_packed_gemv: Y[b][r] = s[r] * sum_c z[r][c] * X[b][c] for b < batch (1..8);
+ *   X batch x n, Y batch x rows, dtype.  args: rows, n, bits, dtype, packed, scales, batch,
+ *   X, Y.  The sum runs in dtype in an order of the kernel's choosing.
+ * Return 0, -i for invalid argument i, or GPTQ2D_ERR_HIP.  No info flag.
+ */
+size_t gptq2d_packed_row_words(int64_t n, int bits);
+int gptq2d_pack(int64_t rows, int64_t n, int bits, const int8_t* codes, uint32_t* packed,
+                void* stream);
+int gptq2d_unpack(int64_t rows, int64_t n, int bits, int dtype, const uint32_t* packed,
+                  const void* scales, void* Q, void* stream);
+int gptq2d_packed_gemv(int64_t rows, int64_t n, int bits, int dtype, const uint32_t* packed,
+                       const void* scales, int batch, const void* X, void* Y, void* stream);
+
+/*
  * Measurement hook (not part of the method): when enabled, every kernel launch of
  * the library is bracketed by a pair of HIP events on its stream and accounted to a
  * kernel class (0 sweep, 2 factor: the persistent Cholesky and inverse, 3 other, 4 the
- * mode-1 feedback between slabs of gptq2d_quantize3) with the
+ * mode-1 feedback between slabs of gptq2d_quantize3, 5 packed: gptq2d_pack, gptq2d_unpack
+ * and gptq2d_packed_gemv) with the
  * algorithmic flops and HBM bytes of that launch.  Class 1 (band_gemm) is counted
  * inside the persistent sweep kernel: its milliseconds are the summed busy time of the
  * workgroups that ran band-update tasks (CU-milliseconds), its launches the tasks and
@@ -146,7 +173,7 @@ size_t gptq2d_workspace3_bytes(int64_t m1, int64_t m2, int64_t m3, int dtype);
  * records to the stream and three atomics per band-update task while on.
  * gptq2d_profile_read waits for the recorded events, writes per-class totals since
  * the previous read (milliseconds, launches, flops, bytes; host arrays, any pointer
- * may be NULL) for the first min(n_classes, 5) classes and resets the totals.
+ * may be NULL) for the first min(n_classes, 6) classes and resets the totals.
  * Returns 0, -1 if n_classes < 0, or GPTQ2D_ERR_HIP if an event query failed.
  */
 int gptq2d_profile_enable(int on);

@@ -99,3 +99,22 @@ def test_three_factor_arguments_rejected_on_host(lib):
     assert lib.gptq2d_workspace3_bytes(4, 4, 4, 3) == 0
     w = lib.gptq2d_workspace3_bytes(16, 1024, 1024, 1)
     assert w % 256 == 0 and w >= 16 * 1024 * 1024 * 8 + 2 * 1024 * 1024 * 8
+
+
+def test_packing_arguments_rejected_on_host(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.gptq2d_packed_row_words(11, 3) == 2
+    assert lib.gptq2d_packed_row_words(4096, 4) == 512
+    assert lib.gptq2d_packed_row_words(0, 4) == 0 and lib.gptq2d_packed_row_words(8, 9) == 0
+    assert lib.gptq2d_pack(0, 4, 4, p, p, None) == -1
+    assert lib.gptq2d_pack(4, 0, 4, p, p, None) == -2
+    assert lib.gptq2d_pack(4, 4, 1, p, p, None) == -3
+    assert lib.gptq2d_pack(4, 4, 4, None, p, None) == -4
+    assert lib.gptq2d_pack(4, 4, 4, p, None, None) == -5
+    assert lib.gptq2d_unpack(4, 4, 4, 3, p, p, p, None) == -4
+    assert lib.gptq2d_unpack(4, 4, 4, 1, p, None, p, None) == -6
+    assert lib.gptq2d_unpack(4, 4, 4, 1, p, p, None, None) == -7
+    assert lib.gptq2d_packed_gemv(4, 4, 4, 1, p, p, 0, p, p, None) == -7
+    assert lib.gptq2d_packed_gemv(4, 4, 4, 1, p, p, 9, p, p, None) == -7
+    assert lib.gptq2d_packed_gemv(4, 4, 4, 1, p, p, 2, None, p, None) == -8
+    assert lib.gptq2d_packed_gemv(4, 4, 4, 1, p, p, 2, p, None, None) == -9

@@ -10,10 +10,13 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     factor,
     load_library,
+    pack,
+    packed_gemv,
     profile_enable,
     profile_read,
     quantize,
     quantize3,
     quantize_factored,
+    unpack,
     workspace_bytes,
 )

@@ -36,6 +36,15 @@ _SYMBOLS = {
                          [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t,
                                                   ctypes.c_void_p, ctypes.c_void_p]),
     "gptq2d_workspace3_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 3 + [ctypes.c_int]),
+    "gptq2d_packed_row_words": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int]),
+    "gptq2d_pack": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p]),
+    "gptq2d_unpack": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int] +
+                      [ctypes.c_void_p] * 4),
+    "gptq2d_packed_gemv": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]),
     "gptq2d_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gptq2d_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "gptq2d_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -208,6 +217,48 @@ def quantize3(W: torch.Tensor, A1: torch.Tensor, A2: torch.Tensor, A3: torch.Ten
     if check:
         _check_info(info)
     return codes, Q
+
+
+def pack(codes: torch.Tensor, bits: int) -> torch.Tensor:
+    """int8 codes (rows, n) -> packed rows (rows, ceil(n*bits/32)) as int32 words
+    (gptq2d_pack; the words are uint32 bit patterns)."""
+    lib = load_library()
+    rows, n = codes.shape
+    _check_dev("codes", codes, torch.int8, (rows, n))
+    P = torch.empty((rows, lib.gptq2d_packed_row_words(n, int(bits))), dtype=torch.int32,
+                    device=codes.device)
+    _raise_rc(lib.gptq2d_pack(rows, n, int(bits), codes.data_ptr(), P.data_ptr(),
+                              _stream(codes.device)), "gptq2d_pack")
+    return P
+
+
+def unpack(P: torch.Tensor, n: int, bits: int, scales: torch.Tensor) -> torch.Tensor:
+    """Q = diag(s) Z from packed rows (gptq2d_unpack), in the dtype of scales."""
+    lib = load_library()
+    rows = P.shape[0]
+    _check_dev("packed", P, torch.int32, (rows, lib.gptq2d_packed_row_words(n, int(bits))))
+    _check_dev("scales", scales, scales.dtype, (rows,))
+    Q = torch.empty((rows, n), dtype=scales.dtype, device=P.device)
+    _raise_rc(lib.gptq2d_unpack(rows, n, int(bits), _dt(scales), P.data_ptr(), scales.data_ptr(),
+                                Q.data_ptr(), _stream(P.device)), "gptq2d_unpack")
+    return Q
+
+
+def packed_gemv(P: torch.Tensor, n: int, bits: int, scales: torch.Tensor, X: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X Q^T for X (batch <= 8, n) with Q = diag(s) Z held packed (gptq2d_packed_gemv)."""
+    lib = load_library()
+    rows = P.shape[0]
+    batch = X.shape[0]
+    _check_dev("packed", P, torch.int32, (rows, lib.gptq2d_packed_row_words(n, int(bits))))
+    _check_dev("scales", scales, scales.dtype, (rows,))
+    _check_dev("X", X, scales.dtype, (batch, n))
+    Y = out if out is not None else torch.empty((batch, rows), dtype=scales.dtype,
+                                                device=P.device)
+    _raise_rc(lib.gptq2d_packed_gemv(rows, n, int(bits), _dt(scales), P.data_ptr(),
+                                     scales.data_ptr(), batch, X.data_ptr(), Y.data_ptr(),
+                                     _stream(P.device)), "gptq2d_packed_gemv")
+    return Y
 
 
 def profile_enable(on: bool = True) -> None:

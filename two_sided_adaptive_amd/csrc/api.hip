@@ -258,6 +258,48 @@ int gptq2d_quantize3(int64_t m1, int64_t m2, int64_t m3, int bits, int dtype, co
                                    ws.ptr, info, s));
 }
 
+size_t gptq2d_packed_row_words(int64_t n, int bits) {
+  if (n <= 0 || n > ((int64_t)1 << 40) || bits < 2 || bits > 8) return 0;
+  return (size_t)g2d::packed_row_words(n, bits);
+}
+
+int gptq2d_pack(int64_t rows, int64_t n, int bits, const int8_t* codes, uint32_t* packed,
+                void* stream) {
+  if (rows <= 0 || rows > ((int64_t)1 << 40)) return -1;
+  if (n <= 0 || n > ((int64_t)1 << 40)) return -2;
+  if (bits < 2 || bits > 8) return -3;
+  if (codes == nullptr) return -4;
+  if (packed == nullptr) return -5;
+  return status(g2d::pack_enqueue(rows, n, bits, codes, packed, (hipStream_t)stream));
+}
+
+int gptq2d_unpack(int64_t rows, int64_t n, int bits, int dtype, const uint32_t* packed,
+                  const void* scales, void* Q, void* stream) {
+  if (rows <= 0 || rows > ((int64_t)1 << 40)) return -1;
+  if (n <= 0 || n > ((int64_t)1 << 40)) return -2;
+  if (bits < 2 || bits > 8) return -3;
+  if (bad_dtype(dtype)) return -4;
+  if (packed == nullptr) return -5;
+  if (scales == nullptr) return -6;
+  if (Q == nullptr) return -7;
+  return status(g2d::unpack_enqueue(rows, n, bits, dtype, packed, scales, Q, (hipStream_t)stream));
+}
+
+int gptq2d_packed_gemv(int64_t rows, int64_t n, int bits, int dtype, const uint32_t* packed,
+                       const void* scales, int batch, const void* X, void* Y, void* stream) {
+  if (rows <= 0 || rows > ((int64_t)1 << 40)) return -1;
+  if (n <= 0 || n > ((int64_t)1 << 40)) return -2;
+  if (bits < 2 || bits > 8) return -3;
+  if (bad_dtype(dtype)) return -4;
+  if (packed == nullptr) return -5;
+  if (scales == nullptr) return -6;
+  if (batch < 1 || batch > 8) return -7;
+  if (X == nullptr) return -8;
+  if (Y == nullptr) return -9;
+  return status(g2d::packed_gemv_enqueue(rows, n, bits, dtype, packed, scales, batch, X, Y,
+                                         (hipStream_t)stream));
+}
+
 int gptq2d_profile_enable(int on) {
   g2d::ProfState& p = g2d::prof();
   std::lock_guard<std::mutex> g(p.mu);
@@ -307,7 +349,7 @@ int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* fl
 
 const char* gptq2d_profile_class_name(int cls) {
   static const char* names[g2d::KC_COUNT] = {"sweep", "band_gemm", "factor", "other",
-                                                  "slab_feedback"};
+                                                  "slab_feedback", "packed"};
   return (cls >= 0 && cls < g2d::KC_COUNT) ? names[cls] : "unknown";
 }
 

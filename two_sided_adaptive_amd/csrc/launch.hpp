@@ -36,4 +36,14 @@ hipError_t kron3_enqueue(int64_t m1, int64_t m2, int64_t m3, int bits, int dtype
                          const void* A1, const void* A2, const void* A3, const void* scales,
                          int8_t* codes, void* Q, void* ws, int* info, hipStream_t s);
 
+// Packed codes (pack.hip): ceil(n*bits/32) uint32 words per row.
+int64_t packed_row_words(int64_t n, int bits);
+hipError_t pack_enqueue(int64_t rows, int64_t n, int bits, const int8_t* codes,
+                        uint32_t* packed, hipStream_t s);
+hipError_t unpack_enqueue(int64_t rows, int64_t n, int bits, int dtype, const uint32_t* packed,
+                          const void* scales, void* Q, hipStream_t s);
+hipError_t packed_gemv_enqueue(int64_t rows, int64_t n, int bits, int dtype,
+                               const uint32_t* packed, const void* scales, int batch,
+                               const void* X, void* Y, hipStream_t s);
+
 }  // namespace g2d

@@ -15,7 +15,8 @@ enum KernelClass : int {
   KC_FACTOR = 2,     // the persistent Cholesky + inverse kernel of the factor stage
   KC_OTHER = 3,      // setup, init and check kernels
   KC_SLAB = 4,       // mode-1 feedback between the slabs of a three-factor tensor
-  KC_COUNT = 5
+  KC_PACK = 5,       // packing of codes, unpacking to Q, and the packed-code GEMV
+  KC_COUNT = 6
 };
 
 bool prof_on();
