@@ -188,6 +188,43 @@ def kron3_leg(steps, warmup, cpu, peak):
     return out
 
 
+def packed_leg(codes, scales, bits, reps, peak):
+    """Packed storage of the layer's codes: pack, unpack to Q, and a batch-1 and batch-8
+    GEMV on the packed rows, each timed with the library's event hook over `reps` calls."""
+    import torch
+
+    import two_sided_adaptive_amd as g2d
+
+    rows, n = codes.shape
+    dev = codes.device
+    P = g2d.pack(codes, bits)
+    X8 = torch.randn((8, n), dtype=scales.dtype, device=dev,
+                     generator=torch.Generator(device=dev).manual_seed(11))
+    Y = torch.empty((8, rows), dtype=scales.dtype, device=dev)
+    out = {"workload": f"{rows}x{n} {bits}-bit codes of the layer, {scales.dtype}",
+           "packed_bytes": int(P.numel() * 4)}
+    calls = {"pack": lambda: g2d.pack(codes, bits),
+             "unpack": lambda: g2d.unpack(P, n, bits, scales),
+             "gemv_b1": lambda: g2d.packed_gemv(P, n, bits, scales, X8[:1], out=Y[:1]),
+             "gemv_b8": lambda: g2d.packed_gemv(P, n, bits, scales, X8, out=Y)}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        g2d.profile_enable(True)
+        g2d.profile_read()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        ms, launches, fl, by = g2d.profile_read()["packed"]
+        g2d.profile_enable(False)
+        us = 1e3 * ms / launches
+        gbs = by / launches / (us * 1e-6) / 1e9
+        out[name] = {"avg_launch_us": us, "bytes_per_launch": by / launches,
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": peak["hbm_gbs"],
+                                  "unit": "GB/s", "frac": gbs / peak["hbm_gbs"]}}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +390,8 @@ def main():
         log(f"[bench] cpu baseline: oracle on the first {args.cpu_rows} rows")
         cpu = cpu_baseline(wl, W.astype(np.float64), A.astype(np.float64),
                            B.astype(np.float64), s.astype(np.float64), z_gpu, args.cpu_rows)
+    log("[bench] packed codes leg")
+    pk = packed_leg(codes, ts, wl.bits, 50, PEAK)
     k3 = None
     if not args.no_kron3:
         log("[bench] three-factor leg (K2)")
@@ -372,6 +411,7 @@ def main():
         "cpu_baseline": cpu,
         "other_dtype": alt,
         "kron3": k3,
+        "packed": pk,
     }
     print(json.dumps(out), flush=True)
 

@@ -150,6 +150,7 @@ size_t gptq2d_workspace3_bytes(int64_t m1, int64_t m2, int64_t m3, int dtype);
  * gptq2d_packed_gemv: Y[b][r] = s[r] * sum_c z[r][c] * X[b][c] for b < batch (1..8);
  *   X batch x n, Y batch x rows, dtype.  args: rows, n, bits, dtype, packed, scales, batch,
  *   X, Y.  The sum runs in dtype in an order of the kernel's choosing.
+ * A row must hold fewer than 2^31 - 32 bits (n * bits); longer rows return GPTQ2D_ERR_HIP.
  * Return 0, -i for invalid argument i, or GPTQ2D_ERR_HIP.  No info flag.
  */
 size_t gptq2d_packed_row_words(int64_t n, int bits);

@@ -46,3 +46,4 @@ from .kron3 import (  # noqa: F401
     quantize3,
     quantize3_factored,
 )
+from . import packing  # noqa: F401,E402
