@@ -29,7 +29,7 @@ def _codes(rows, n, bits, seed):
     return z.astype(np.int8)
 
 
-SHAPES = [(1, 1), (3, 31), (5, 33), (7, 100), (65, 1000), (130, 4099)]
+SHAPES = [(1, 1), (3, 31), (5, 33), (7, 100), (65, 1000), (130, 4099), (9, 4096)]
 
 
 @pytest.mark.parametrize("bits", range(2, 9))

@@ -23,7 +23,10 @@ namespace {
 // from the int8 codes (adjacent threads read adjacent code ranges) and assembled; a field
 // that straddles two words gives its low part to the first and its high part to the second.
 // Codes outside [lo, hi] are stored modulo 2^bits.
-template <int BITS>
+// With VEC (bits 2, 4 or 8, whose fields never straddle words, a row length that is a
+// multiple of 32/bits and aligned codes, checked on the host) the word's 32/bits codes are
+// one vector load.
+template <int BITS, bool VEC>
 __global__ __launch_bounds__(256) void k_pack(const int8_t* __restrict__ codes,
                                               uint32_t* __restrict__ packed, int64_t rows,
                                               int n, int wpr) {
@@ -31,6 +34,18 @@ __global__ __launch_bounds__(256) void k_pack(const int8_t* __restrict__ codes,
   constexpr unsigned mask = (1u << BITS) - 1u;
   const int w = blockIdx.x * 256 + threadIdx.x;
   if (w >= wpr) return;
+  if constexpr (VEC && 32 % BITS == 0) {
+    constexpr int K = 32 / BITS;  // codes per word: 16, 8 or 4 bytes
+    typedef int8_t vec_t __attribute__((ext_vector_type(K)));
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+      const vec_t v = *(const vec_t*)(codes + r * n + (int64_t)w * K);
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < K; ++k) word |= ((unsigned)((int)v[k] - lo) & mask) << (k * BITS);
+      packed[r * wpr + w] = word;
+    }
+    return;
+  }
   const int bit0 = 32 * w;
   const int c0 = bit0 / BITS;                           // first field overlapping the word
   const int c1 = min((bit0 + 32 + BITS - 1) / BITS, n);  // one past the last one
@@ -175,8 +190,12 @@ template <int BITS>
 struct PackLaunch {
   static hipError_t run(int64_t rows, int n, int wpr, const int8_t* codes, uint32_t* packed,
                         hipStream_t s) {
-    k_pack<BITS><<<dim3((unsigned)cdiv(wpr, 256), grid_rows(rows)), 256, 0, s>>>(codes, packed,
-                                                                              rows, n, wpr);
+    const dim3 grid((unsigned)cdiv(wpr, 256), grid_rows(rows));
+    const int K = 32 / BITS;
+    if (32 % BITS == 0 && n % K == 0 && (uintptr_t)codes % K == 0)
+      k_pack<BITS, true><<<grid, 256, 0, s>>>(codes, packed, rows, n, wpr);
+    else
+      k_pack<BITS, false><<<grid, 256, 0, s>>>(codes, packed, rows, n, wpr);
     return hipGetLastError();
   }
 };
