@@ -25,6 +25,8 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
     unpack_rows          nibble views for 8 and 4 bits, round trip, zero padding
   packing.dequantize /   pinned: equals the quantizer's Q; explicit dot products
     packed_gemv
+  gram.gram_accumulate   pinned: sum of outer products, exact integer case,
+                         symmetry and positive semi-definiteness
 """
 from .gptq2d import (  # noqa: F401
     babai_nearest_plane,
@@ -47,3 +49,4 @@ from .kron3 import (  # noqa: F401
     quantize3_factored,
 )
 from . import packing  # noqa: F401,E402
+from . import gram  # noqa: F401,E402
