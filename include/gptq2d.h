@@ -162,11 +162,33 @@ int gptq2d_packed_gemv(int64_t rows, int64_t n, int bits, int dtype, const uint3
                        const void* scales, int batch, const void* X, void* Y, void* stream);
 
 /*
+ * Kronecker factor accumulation, the step before the quantizer: the pages take the
+ * factors of a Kronecker-factored Hessian as given ("GPTQ-2D: Cubic-Time Two-Sided
+ * Adaptive Rounding", arxivlens page, Abstract) and do not say how they are estimated;
+ * this is the plain second-moment (Gram) accumulation over a block of samples:
+ *   A <- A + alpha * X^T X,   X: N x p (N samples of dimension p, row-major), A: p x p.
+ * A must be symmetric on entry: its lower triangle (diagonal included) is read and updated,
+ * then copied onto the upper triangle, so A leaves symmetric.  Both in `dtype`; the sums
+ * run in dtype on the matrix cores in an order of the kernel's choosing.  p in [1, 262140]
+ * with p*p*sizeof(dtype) < 2^31 (else GPTQ2D_ERR_HIP); N >= 1; alpha finite.
+ *   args: p, N, dtype, X, alpha, A, stream
+ * gptq2d_gram_accumulate_batched: the same for `count` layers in one call (host arrays of
+ * length count: p, N, X, alpha, A), enqueued in order on `stream`; an invalid entry of an
+ * array returns the index of that array argument.
+ *   args: count, p, N, dtype, X, alpha, A, stream
+ */
+int gptq2d_gram_accumulate(int64_t p, int64_t N, int dtype, const void* X, double alpha,
+                           void* A, void* stream);
+int gptq2d_gram_accumulate_batched(int count, const int64_t* p, const int64_t* N, int dtype,
+                                   const void* const* X, const double* alpha, void* const* A,
+                                   void* stream);
+
+/*
  * Measurement hook (not part of the method): when enabled, every kernel launch of
  * the library is bracketed by a pair of HIP events on its stream and accounted to a
  * kernel class (0 sweep, 2 factor: the persistent Cholesky and inverse, 3 other, 4 the
  * mode-1 feedback between slabs of gptq2d_quantize3, 5 packed: gptq2d_pack, gptq2d_unpack
- * and gptq2d_packed_gemv) with the
+ * and gptq2d_packed_gemv, 6 gram: gptq2d_gram_accumulate) with the
  * algorithmic flops and HBM bytes of that launch.  Class 1 (band_gemm) is counted
  * inside the persistent sweep kernel: its milliseconds are the summed busy time of the
  * workgroups that ran band-update tasks (CU-milliseconds), its launches the tasks and
@@ -174,7 +196,7 @@ int gptq2d_packed_gemv(int64_t rows, int64_t n, int bits, int dtype, const uint3
  * records to the stream and three atomics per band-update task while on.
  * gptq2d_profile_read waits for the recorded events, writes per-class totals since
  * the previous read (milliseconds, launches, flops, bytes; host arrays, any pointer
- * may be NULL) for the first min(n_classes, 6) classes and resets the totals.
+ * may be NULL) for the first min(n_classes, 7) classes and resets the totals.
  * Returns 0, -1 if n_classes < 0, or GPTQ2D_ERR_HIP if an event query failed.
  */
 int gptq2d_profile_enable(int on);

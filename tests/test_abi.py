@@ -118,3 +118,23 @@ def test_packing_arguments_rejected_on_host(lib):
     assert lib.gptq2d_packed_gemv(4, 4, 4, 1, p, p, 9, p, p, None) == -7
     assert lib.gptq2d_packed_gemv(4, 4, 4, 1, p, p, 2, None, p, None) == -8
     assert lib.gptq2d_packed_gemv(4, 4, 4, 1, p, p, 2, p, None, None) == -9
+
+
+def test_gram_arguments_rejected_on_host(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.gptq2d_gram_accumulate(0, 4, 1, p, 1.0, p, None) == -1
+    assert lib.gptq2d_gram_accumulate(4, 0, 1, p, 1.0, p, None) == -2
+    assert lib.gptq2d_gram_accumulate(4, 4, 2, p, 1.0, p, None) == -3
+    assert lib.gptq2d_gram_accumulate(4, 4, 1, None, 1.0, p, None) == -4
+    assert lib.gptq2d_gram_accumulate(4, 4, 1, p, float("nan"), p, None) == -5
+    assert lib.gptq2d_gram_accumulate(4, 4, 1, p, float("inf"), p, None) == -5
+    assert lib.gptq2d_gram_accumulate(4, 4, 1, p, 1.0, None, None) == -6
+    P = (ctypes.c_int64 * 2)(4, 0)
+    N = (ctypes.c_int64 * 2)(3, 3)
+    X = (ctypes.c_void_p * 2)(16, 16)
+    al = (ctypes.c_double * 2)(1.0, 1.0)
+    assert lib.gptq2d_gram_accumulate_batched(0, P, N, 1, X, al, X, None) == -1
+    assert lib.gptq2d_gram_accumulate_batched(2, P, N, 1, X, al, X, None) == -2   # p[1] = 0
+    P[1] = 4
+    assert lib.gptq2d_gram_accumulate_batched(2, P, N, 7, X, al, X, None) == -4
+    assert lib.gptq2d_gram_accumulate_batched(2, P, N, 1, None, al, X, None) == -5

@@ -9,6 +9,8 @@ from ._binding import (  # noqa: F401
     GPTQ2DError,
     LIB_PATH,
     factor,
+    gram_accumulate,
+    gram_accumulate_batched,
     load_library,
     pack,
     packed_gemv,

@@ -36,6 +36,13 @@ _SYMBOLS = {
                          [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t,
                                                   ctypes.c_void_p, ctypes.c_void_p]),
     "gptq2d_workspace3_bytes": (ctypes.c_size_t, [ctypes.c_int64] * 3 + [ctypes.c_int]),
+    "gptq2d_gram_accumulate": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
+                                              ctypes.c_void_p]),
+    "gptq2d_gram_accumulate_batched": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p,
+                                                      ctypes.c_void_p, ctypes.c_int,
+                                                      ctypes.c_void_p, ctypes.c_void_p,
+                                                      ctypes.c_void_p, ctypes.c_void_p]),
     "gptq2d_packed_row_words": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int]),
     "gptq2d_pack": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_void_p]),
@@ -259,6 +266,38 @@ def packed_gemv(P: torch.Tensor, n: int, bits: int, scales: torch.Tensor, X: tor
                                      scales.data_ptr(), batch, X.data_ptr(), Y.data_ptr(),
                                      _stream(P.device)), "gptq2d_packed_gemv")
     return Y
+
+
+def gram_accumulate(A: torch.Tensor, X: torch.Tensor, alpha: float = 1.0) -> torch.Tensor:
+    """A += alpha X^T X in place (gptq2d_gram_accumulate); X (N, p), A (p, p) symmetric."""
+    lib = load_library()
+    N, p = X.shape
+    _check_dev("X", X, X.dtype, (N, p))
+    _check_dev("A", A, X.dtype, (p, p))
+    _raise_rc(lib.gptq2d_gram_accumulate(p, N, _dt(X), X.data_ptr(), float(alpha), A.data_ptr(),
+                                         _stream(X.device)), "gptq2d_gram_accumulate")
+    return A
+
+
+def gram_accumulate_batched(As, Xs, alphas) -> None:
+    """Several layers in one call (gptq2d_gram_accumulate_batched), each A += alpha X^T X."""
+    import numpy as np
+    lib = load_library()
+    cnt = len(As)
+    if not (len(Xs) == len(alphas) == cnt) or cnt == 0:
+        raise ValueError("As, Xs and alphas must have the same non-zero length")
+    dt = _dt(Xs[0])
+    for A, X in zip(As, Xs):
+        _check_dev("X", X, Xs[0].dtype, tuple(X.shape))
+        _check_dev("A", A, Xs[0].dtype, (X.shape[1], X.shape[1]))
+    p = np.array([X.shape[1] for X in Xs], dtype=np.int64)
+    n = np.array([X.shape[0] for X in Xs], dtype=np.int64)
+    xp = (ctypes.c_void_p * cnt)(*[X.data_ptr() for X in Xs])
+    ap = (ctypes.c_void_p * cnt)(*[A.data_ptr() for A in As])
+    al = np.array(alphas, dtype=np.float64)
+    _raise_rc(lib.gptq2d_gram_accumulate_batched(cnt, p.ctypes.data, n.ctypes.data, dt, xp,
+                                                 al.ctypes.data, ap, _stream(Xs[0].device)),
+              "gptq2d_gram_accumulate_batched")
 
 
 def profile_enable(on: bool = True) -> None:

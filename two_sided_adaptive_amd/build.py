@@ -10,7 +10,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["api.hip", "factor.hip", "sweep.hip", "kron3.hip", "pack.hip"]
+SOURCES = ["api.hip", "factor.hip", "sweep.hip", "kron3.hip", "pack.hip", "gram.hip"]
 HEADERS = ["common.hpp", "launch.hpp", "prof.hpp"]
 LIB = os.path.join(PKG, "libgptq2d.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

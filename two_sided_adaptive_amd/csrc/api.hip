@@ -300,6 +300,42 @@ int gptq2d_packed_gemv(int64_t rows, int64_t n, int bits, int dtype, const uint3
                                          (hipStream_t)stream));
 }
 
+int gptq2d_gram_accumulate(int64_t p, int64_t N, int dtype, const void* X, double alpha,
+                           void* A, void* stream) {
+  if (p <= 0 || p > kMaxDim) return -1;
+  if (N <= 0) return -2;
+  if (bad_dtype(dtype)) return -3;
+  if (X == nullptr) return -4;
+  if (!(alpha == alpha) || alpha == 1.0 / 0.0 || alpha == -1.0 / 0.0) return -5;
+  if (A == nullptr) return -6;
+  return status(g2d::gram_enqueue(p, N, dtype, X, alpha, A, (hipStream_t)stream));
+}
+
+int gptq2d_gram_accumulate_batched(int count, const int64_t* p, const int64_t* N, int dtype,
+                                   const void* const* X, const double* alpha, void* const* A,
+                                   void* stream) {
+  if (count <= 0) return -1;
+  if (p == nullptr) return -2;
+  if (N == nullptr) return -3;
+  if (bad_dtype(dtype)) return -4;
+  if (X == nullptr) return -5;
+  if (alpha == nullptr) return -6;
+  if (A == nullptr) return -7;
+  for (int l = 0; l < count; ++l) {
+    if (p[l] <= 0 || p[l] > kMaxDim) return -2;
+    if (N[l] <= 0) return -3;
+    if (X[l] == nullptr) return -5;
+    if (!(alpha[l] == alpha[l]) || alpha[l] == 1.0 / 0.0 || alpha[l] == -1.0 / 0.0) return -6;
+    if (A[l] == nullptr) return -7;
+  }
+  for (int l = 0; l < count; ++l) {
+    const hipError_t e = g2d::gram_enqueue(p[l], N[l], dtype, X[l], alpha[l], A[l],
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return status(e);
+  }
+  return 0;
+}
+
 int gptq2d_profile_enable(int on) {
   g2d::ProfState& p = g2d::prof();
   std::lock_guard<std::mutex> g(p.mu);
@@ -349,7 +385,7 @@ int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* fl
 
 const char* gptq2d_profile_class_name(int cls) {
   static const char* names[g2d::KC_COUNT] = {"sweep", "band_gemm", "factor", "other",
-                                                  "slab_feedback", "packed"};
+                                                  "slab_feedback", "packed", "gram"};
   return (cls >= 0 && cls < g2d::KC_COUNT) ? names[cls] : "unknown";
 }
 

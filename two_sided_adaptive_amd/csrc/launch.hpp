@@ -46,4 +46,8 @@ hipError_t packed_gemv_enqueue(int64_t rows, int64_t n, int bits, int dtype,
                                const uint32_t* packed, const void* scales, int batch,
                                const void* X, void* Y, hipStream_t s);
 
+// Kronecker factor accumulation (gram.hip): A (p x p, symmetric) += alpha X^T X, X N x p.
+hipError_t gram_enqueue(int64_t p, int64_t N, int dtype, const void* X, double alpha, void* A,
+                        hipStream_t s);
+
 }  // namespace g2d

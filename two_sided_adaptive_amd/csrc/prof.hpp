@@ -16,7 +16,8 @@ enum KernelClass : int {
   KC_OTHER = 3,      // setup, init and check kernels
   KC_SLAB = 4,       // mode-1 feedback between the slabs of a three-factor tensor
   KC_PACK = 5,       // packing of codes, unpacking to Q, and the packed-code GEMV
-  KC_COUNT = 6
+  KC_GRAM = 6,       // Kronecker factor accumulation A += alpha X^T X (and its mirror pass)
+  KC_COUNT = 7
 };
 
 bool prof_on();
