@@ -225,6 +225,35 @@ def packed_leg(codes, scales, bits, reps, peak):
     return out
 
 
+def gram_leg(reps, peak):
+    """Kronecker factor accumulation A += X^T X / N at the layer's width (p = 4096) from
+    N = 8192 synthetic activation samples, fp64, timed with the event hook."""
+    import torch
+
+    import two_sided_adaptive_amd as g2d
+
+    p, N = 4096, 8192
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(12)
+    X = torch.randn((N, p), dtype=torch.float64, device=dev, generator=gen)
+    A = torch.zeros((p, p), dtype=torch.float64, device=dev)
+    g2d.gram_accumulate(A, X, 1.0 / N)
+    torch.cuda.synchronize()
+    g2d.profile_enable(True)
+    g2d.profile_read()
+    for _ in range(reps):
+        g2d.gram_accumulate(A, X, 1.0 / N)
+    torch.cuda.synchronize()
+    ms, launches, fl, by = g2d.profile_read()["gram"]
+    g2d.profile_enable(False)
+    sec = ms / 1e3 / launches
+    tf = fl / launches / sec / 1e12
+    return {"workload": f"A += X^T X / N, p={p}, N={N} samples, fp64",
+            "ms_per_call": sec * 1e3, "flops_per_call": fl / launches,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": peak["fp64_tflops"],
+                         "unit": "TFLOP/s", "frac": tf / peak["fp64_tflops"]}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +421,8 @@ def main():
                            B.astype(np.float64), s.astype(np.float64), z_gpu, args.cpu_rows)
     log("[bench] packed codes leg")
     pk = packed_leg(codes, ts, wl.bits, 50, PEAK)
+    log("[bench] factor accumulation leg")
+    gr = gram_leg(5, PEAK)
     k3 = None
     if not args.no_kron3:
         log("[bench] three-factor leg (K2)")
@@ -412,6 +443,7 @@ def main():
         "other_dtype": alt,
         "kron3": k3,
         "packed": pk,
+        "gram": gr,
     }
     print(json.dumps(out), flush=True)
 
