@@ -6,4 +6,5 @@ CPU oracle and the GPU library can both consume its arrays without sharing any
 code of the method itself.
 """
 from .configs import (  # noqa: F401
-    CONFIG_NAMES, SHAPES3, Workload, Workload3, make, make3, make_random, make_random3)
+    CONFIG_NAMES, SHAPES3, Workload, Workload3, make, make3, make_conditioned, make_random,
+    make_random3)

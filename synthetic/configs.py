@@ -330,3 +330,15 @@ def make_random3(m1: int, m2: int, m3: int, bits: int = 4, seed: int = 0,
     a3 = _wishart_iid(g3, m3, max(m3, 8), 0.05)
     return _finish3(f"rand3_{m1}x{m2}x{m3}b{bits}s{seed}{kind}", w, a1, a2, a3, bits, dtype,
                     f"random3 {kind}")
+
+
+def make_conditioned(p: int, damp: float, bits: int = 4, seed: int = 0) -> Workload:
+    """Square p x p layer whose metrics A, B = U diag(k^-1.5) U^T + damp * I (Haar U, as in
+    the 512-wide layer) have condition number about 1/damp: the precision study's inputs."""
+    gw, ga, gb, _ = _streams(30_000 + seed)
+    w = 0.02 * gw.standard_normal((p, p))
+    a = _spectral(ga, p, 1.5, damp)
+    b = _spectral(gb, p, 1.5, damp)
+    return _finish(f"cond{p}d{damp:g}", w, a, b, bits, "f32",
+                   f"{p}x{p}; W~N(0,0.02^2); A,B = U diag(k^-1.5) U^T + {damp:g} I (Haar U); "
+                   f"{bits}-bit")
