@@ -139,3 +139,21 @@ def test_numerical_failures_reported(g2d):
     # the library still works afterwards
     (W, A, B, s), z, _ = _run(g2d, wl, "f64")
     assert np.array_equal(z, oracle.quantize(W, A, B, s, 4)["Z"])
+
+
+@pytest.mark.parametrize("shape", [(130, 200), (200, 130), (257, 129), (65, 63)])
+def test_workspace_contents_do_not_matter(g2d, shape):
+    # a caller's workspace may hold anything, NaN included: the codes must not depend on it
+    m, n = shape
+    bits = 2 + (m * 7 + n) % 7
+    wl = make_random(m, n, bits, seed=m * 1000 + n)
+    W, A, B, s = wl.cast("f64")
+    ref = oracle.quantize(W, A, B, s, bits)
+    tW, tA, tB, ts = _dev(W, A, B, s)
+    need = g2d.workspace_bytes(m, n, torch.float64)
+    for fill in (float("nan"), float("inf"), 0.0):
+        print(f"case workspace fill {fill} m={m} n={n}", flush=True)
+        ws = torch.full((need // 8 + 1,), fill, dtype=torch.float64, device=DEV)
+        codes, Q = g2d.quantize(tW, tA, tB, bits, ts, workspace=ws.view(torch.uint8)[:need])
+        z = codes.cpu().numpy().astype(np.int32)
+        assert np.array_equal(z, ref["Z"]), f"fill {fill}: {int(np.sum(z != ref['Z']))} mismatches"

@@ -461,11 +461,20 @@ __device__ inline void tile_loads(const SweepArgs<T>& a, int K, int w, int j, in
   const int rows = mr - MU * w;  // (<= 0 for a wave without rows: nothing is read)
   const int64_t tile_bytes = rows > 0 ? ((int64_t)(rows - 1) * n + nc) * es : 0;
   const int64_t o0 = rows > 0 ? row0 * n + c0 : 0;
+  // A lane whose column lies past n reads, inside the tile's range, the first columns of the
+  // next row, which may never have been written (an accumulator that no contribution
+  // reaches) and may hold anything, NaN included.  Such a lane's values only reach outputs
+  // that are never stored, except through a product with a zero coefficient (the in-tile
+  // horizontal feedback multiplies every column of the micro-tile), where a NaN would
+  // survive: so they are set to zero.
+  const bool col_ok = cl < nc;
   if (parts & 1) {
     const rsrc_t rw = make_rsrc(a.W + o0, tile_bytes);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      ld.win[e] = buf_load<T>(rw, (uint32_t)(Mfma<T>::row(lane, e) * n + cl));
+    for (int e = 0; e < 4; ++e) {
+      const T v = buf_load<T>(rw, (uint32_t)(Mfma<T>::row(lane, e) * n + cl));
+      ld.win[e] = col_ok ? v : T(0);
+    }
   }
   if (parts & 2) {
 #pragma unroll
@@ -477,8 +486,9 @@ __device__ inline void tile_loads(const SweepArgs<T>& a, int K, int w, int j, in
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t o = (uint32_t)(Mfma<T>::row(lane, e) * n + cl);
-        ld.vf[c][e] = buf_load_dev<T>(rvf, o);
-        ld.hf[c][e] = buf_load_dev<T>(rhf, o);
+        const T vv = buf_load_dev<T>(rvf, o), hv = buf_load_dev<T>(rhf, o);
+        ld.vf[c][e] = col_ok ? vv : T(0);
+        ld.hf[c][e] = col_ok ? hv : T(0);
       }
     }
   } else {
