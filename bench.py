@@ -304,6 +304,9 @@ def main():
     ap.add_argument("--no-alt", action="store_true", help="skip timing the other sweep dtype")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-precision", action="store_true",
+                    help="skip the precision study (its 1024-wide sweeps would mix into a "
+                         "profile of the headline sweep)")
     ap.add_argument("--no-kron3", action="store_true",
                     help="skip the three-factor tensor leg (K2, 16x1024x1024)")
     ap.add_argument("--kron3-only", action="store_true",
@@ -461,8 +464,10 @@ def main():
     pk = packed_leg(codes, ts, wl.bits, 50, PEAK)
     log("[bench] factor accumulation leg")
     gr = gram_leg(5, PEAK)
-    log("[bench] precision study leg")
-    prec = precision_leg()
+    prec = None
+    if not args.no_precision:
+        log("[bench] precision study leg")
+        prec = precision_leg()
     k3 = None
     if not args.no_kron3:
         log("[bench] three-factor leg (K2)")

@@ -461,20 +461,11 @@ __device__ inline void tile_loads(const SweepArgs<T>& a, int K, int w, int j, in
   const int rows = mr - MU * w;  // (<= 0 for a wave without rows: nothing is read)
   const int64_t tile_bytes = rows > 0 ? ((int64_t)(rows - 1) * n + nc) * es : 0;
   const int64_t o0 = rows > 0 ? row0 * n + c0 : 0;
-  // A lane whose column lies past n reads, inside the tile's range, the first columns of the
-  // next row, which may never have been written (an accumulator that no contribution
-  // reaches) and may hold anything, NaN included.  Such a lane's values only reach outputs
-  // that are never stored, except through a product with a zero coefficient (the in-tile
-  // horizontal feedback multiplies every column of the micro-tile), where a NaN would
-  // survive: so they are set to zero.
-  const bool col_ok = cl < nc;
   if (parts & 1) {
     const rsrc_t rw = make_rsrc(a.W + o0, tile_bytes);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const T v = buf_load<T>(rw, (uint32_t)(Mfma<T>::row(lane, e) * n + cl));
-      ld.win[e] = col_ok ? v : T(0);
-    }
+    for (int e = 0; e < 4; ++e)
+      ld.win[e] = buf_load<T>(rw, (uint32_t)(Mfma<T>::row(lane, e) * n + cl));
   }
   if (parts & 2) {
 #pragma unroll
@@ -486,9 +477,8 @@ __device__ inline void tile_loads(const SweepArgs<T>& a, int K, int w, int j, in
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t o = (uint32_t)(Mfma<T>::row(lane, e) * n + cl);
-        const T vv = buf_load_dev<T>(rvf, o), hv = buf_load_dev<T>(rhf, o);
-        ld.vf[c][e] = col_ok ? vv : T(0);
-        ld.hf[c][e] = col_ok ? hv : T(0);
+        ld.vf[c][e] = buf_load_dev<T>(rvf, o);
+        ld.hf[c][e] = buf_load_dev<T>(rhf, o);
       }
     }
   } else {
@@ -1227,6 +1217,24 @@ __global__ __launch_bounds__(256) void k_init_sync(int* p, int64_t words) {
     p[i] = 0;
 }
 
+// When n is not a multiple of the micro-tile width, the lanes of a row's last micro-tile
+// whose columns lie past n read, inside the tile's buffer range, the first columns of the
+// next row.  Their values only reach outputs that are never stored, except through a
+// product with a zero coefficient (the in-tile horizontal feedback multiplies every column
+// of the micro-tile), where a NaN would survive.  The horizontal accumulators' first
+// columns belong to column block 0, to which no contribution is ever pushed, so they would
+// hold whatever the workspace held: they are cleared here, before the sweep.
+template <typename T>
+__global__ __launch_bounds__(256) void k_clear_lead(T* h0, T* h1, T* h2, int64_t m, int64_t n,
+                                                    int cols) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= m * cols) return;
+  const int64_t o = (i / cols) * n + i % cols;
+  h0[o] = T(0);
+  h1[o] = T(0);
+  h2[o] = T(0);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_check_scales(int64_t m, const T* __restrict__ s,
                                                       int* info) {
@@ -1336,6 +1344,12 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   k_check_scales<T><<<(unsigned)cdiv(m, 256), 256, 0, s>>>(m, scales, info);
   const int64_t ig = cdiv(sl.words, 256) < 4096 ? cdiv(sl.words, 256) : 4096;
   k_init_sync<<<(unsigned)ig, 256, 0, s>>>(sync, sl.words);
+  if (n % MU != 0) {
+    static_assert(NCLS == 3, "one accumulator per class");
+    const int cols = n < MU ? (int)n : MU;
+    k_clear_lead<T><<<(unsigned)cdiv(m * cols, 256), 256, 0, s>>>(a.Hacc[0], a.Hacc[1],
+                                                                   a.Hacc[2], m, n, cols);
+  }
   prof_end(KC_OTHER, s, 0.0, 4.0 * (double)sl.words + es * (double)m);
   // algorithmic work of the sweep: every entry takes its k vertical and l horizontal
   // feedback terms (2 flops each); HBM bytes: W, the factors and scales in, codes and
