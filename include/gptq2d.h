@@ -34,9 +34,15 @@
  *     not positive definite, 2 if B is not, 3 if a scale is <= 0 or not finite,
  *     4 if a dependency wait inside one of the persistent kernels (the sweep, or the
  *     factor stage's Cholesky and inverse) exceeded its bound (the kernel then stops early
- *     instead of hanging; this only happens when the device cannot keep the kernel's
- *     workgroups resident); info[1] = 1-based index
- *     of the failing pivot or row.  When info[0] != 0 the outputs are undefined.
+ *     instead of hanging); info[1] = 1-based index of the failing pivot or row.  When
+ *     info[0] != 0 the outputs are undefined.
+ *   - Limit of every call that factors or sweeps: its persistent kernels launch one grid of
+ *     (compute units x resident workgroups per CU) and need all of it resident at once,
+ *     spread over the device's XCDs by the hardware's round-robin dispatch (the sweep
+ *     deals bands to XCDs and needs band workers on each of them).  Another kernel that
+ *     occupies compute units during the call, or a device partition whose dispatch does not
+ *     spread workgroups over its XCDs, can leave a dependency unserved: the call then ends
+ *     with info[0] = 4 after the wait bound (of the order of seconds), not with a hang.
  *   - workspace: DEVICE scratch of at least the size returned by the matching
  *     *_workspace_bytes function, 256-byte aligned.  Passing NULL and 0 makes the
  *     library allocate (and free) it stream-ordered on `stream`.

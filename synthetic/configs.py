@@ -81,6 +81,24 @@ def _haar(rng: np.random.Generator, p: int) -> np.ndarray:
     return q
 
 
+def _exact_gram(x: np.ndarray, frac_bits: int) -> np.ndarray:
+    """X^T X of the samples rounded to multiples of 2^-frac_bits, computed exactly.
+
+    The rounded samples are integers times 2^-frac_bits; while N * max|X|^2 * 4^frac_bits
+    stays below 2^53 every product and partial sum of the integer Gram is exact in float64,
+    so the result does not depend on the BLAS summation order, the thread count or the
+    CPU.  Only a sample lying within rounding error of a grid midpoint could round
+    differently on another machine, which the fine grid makes rare.  The rounding moves a
+    sample by at most 2^-(frac_bits+1), far below the damping that is added afterwards.
+    """
+    xi = np.rint(np.ldexp(x, frac_bits))
+    big = float(np.max(np.abs(xi))) if xi.size else 0.0
+    if big * big * x.shape[0] >= 2.0 ** 53:
+        raise ValueError("samples too large for an exact Gram at this grid")
+    g = xi.T @ xi
+    return np.ldexp(g, -2 * frac_bits)
+
+
 def _spectral(rng: np.random.Generator, p: int, power: float, damp: float) -> np.ndarray:
     """U diag(k^-power) U^T + damp * I with U Haar (config C2)."""
     u = _haar(rng, p)
@@ -96,7 +114,7 @@ def _wishart_ar1(rng: np.random.Generator, p: int, samples: int, rho: float) -> 
     c = np.sqrt(1.0 - rho * rho)
     for j in range(1, p):
         x[:, j] = rho * x[:, j - 1] + c * z[:, j]
-    a = _sym(x.T @ x) / samples
+    a = _exact_gram(x, 16) / samples
     return a + 0.01 * np.mean(np.diag(a)) * np.eye(p)
 
 
@@ -107,7 +125,7 @@ def _wishart_powerlaw(rng: np.random.Generator, p: int, samples: int, power: flo
     z = rng.standard_normal((samples, p))
     x = (z * np.sqrt(lam)[None, :]) @ u.T
     del z, u
-    a = _sym(x.T @ x) / samples
+    a = _exact_gram(x, 15) / samples
     return a + 0.01 * np.mean(np.diag(a)) * np.eye(p)
 
 
@@ -213,6 +231,22 @@ SHAPES = {"C1": (32, 32, 4), "C2": (512, 512, 4), "C3": (4096, 4096, 4),
           "C4": (14336, 4096, 4), "C4T": (4096, 14336, 4), "C5": (8192, 8192, 3)}
 
 
+# The most recently built large workloads, kept in memory: the transposed 14336-wide layer
+# is built from the untransposed one, and a test process asks for each several times.
+_MEMO: Dict[str, Workload] = {}
+_MEMO_KEEP = 2
+
+
+def _memo_put(name: str, wl: Workload) -> None:
+    if wl.W.size < (1 << 22):
+        return
+    for x in (wl.W, wl.A, wl.B, wl.scales):
+        x.flags.writeable = False  # shared by every caller: modify copies only
+    _MEMO[name] = wl
+    while len(_MEMO) > _MEMO_KEEP:
+        _MEMO.pop(next(iter(_MEMO)))
+
+
 def make(name: str, cache_dir: Optional[str] = None) -> Workload:
     """Build workload `name` (deterministic).  With `cache_dir`, reuse an .npz cache."""
     if name not in _BUILDERS:
@@ -225,7 +259,10 @@ def make(name: str, cache_dir: Optional[str] = None) -> Workload:
             z = np.load(path)
             return Workload(name, z["W"], z["A"], z["B"], z["scales"], int(z["bits"]),
                             str(z["dtype"]), str(z["recipe"]))
+    if name in _MEMO:
+        return _MEMO[name]
     wl = _BUILDERS[name]()
+    _memo_put(name, wl)
     if path:
         tmp = path + ".tmp.npz"
         np.savez(tmp, W=wl.W, A=wl.A, B=wl.B, scales=wl.scales, bits=wl.bits,

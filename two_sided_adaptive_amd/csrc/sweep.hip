@@ -59,7 +59,9 @@ constexpr int FAR_OFF = 2;
 constexpr int kPanel = 2;   // target blocks per GEMM task
 constexpr int kThreads = 256;
 constexpr int kSpinLimit = 1 << 22;
-constexpr int NXCD = 8;     // accelerator complex dies (XCDs) of the MI355X, one L2 each
+// accelerator complex dies (XCDs), one L2 each: 8 on an MI355X in its default partition
+// mode; the count of the device in use is queried at launch (SweepArgs::nxcd)
+constexpr int kMaxXcd = 16;
 
 // control words at the start of the sync area; the per-XCD words sit on their own
 // 128-byte lines
@@ -69,8 +71,8 @@ enum Ctl : int {
   kHead = kLine,                    // + kLine c: next slot of queue c to claim
   kTail = kLine * 4,                // + kLine c: slots of queue c reserved by producers
   kBandX = kLine * 7,               // + kLine x: bands claimed by workgroups on XCD x
-  kXTicket = kLine * (7 + NXCD),    // + kLine x: workgroups started on XCD x
-  kCtlWords = kLine * (7 + 2 * NXCD)
+  kXTicket = kLine * (7 + kMaxXcd),    // + kLine x: workgroups started on XCD x
+  kCtlWords = kLine * (7 + 2 * kMaxXcd)
 };
 // Band-update contributions come in three classes, each with its own accumulators,
 // contribution counters, task queue and workers:
@@ -92,6 +94,7 @@ struct SweepArgs {
   int64_t m, n;
   int Mb, Nb, Nj, lo, hi, bits;
   int qcap[NCLS]; // band-update tasks of each class in the whole sweep
+  int nxcd;   // XCDs of the device (<= kMaxXcd)
   int nbxcd;  // band workers per XCD
   int gs;     // bands are dealt to the XCDs in groups of gs consecutive bands
   const T* Ua;
@@ -193,7 +196,11 @@ __device__ inline void st_dev(int* p, int v) {
 }
 __device__ inline bool aborted(const int* ctl) { return ld_dev(ctl + kAbort) != 0; }
 // XCD (accelerator complex die) this wave runs on: hardware register XCC_ID
-__device__ inline int xcd_id() { return (int)__builtin_amdgcn_s_getreg((3 << 11) | 20) % NXCD; }
+// (hardware register XCC_ID; a partition of the device numbers its XCDs from any base, so
+// the id is taken modulo the partition's XCD count)
+__device__ inline int xcd_id(int nxcd) {
+  return (int)__builtin_amdgcn_s_getreg((3 << 11) | 20) % nxcd;
+}
 __device__ inline void abort_sweep(int* ctl, int* info) {
   if (atomicCAS(ctl + kAbort, 0, 1) == 0) record_info(info, 4, 0);
 }
@@ -827,8 +834,8 @@ __device__ __attribute__((always_inline)) inline void band_worker(const SweepArg
     if (tid == 0) {
       int K = a.Mb;
       if (!aborted(a.ctl)) {
-        const int x = xcd_id(), c = atomicAdd(a.ctl + kBandX + kLine * x, 1);
-        K = a.gs * (x + NXCD * (c / a.gs)) + c % a.gs;
+        const int x = xcd_id(a.nxcd), c = atomicAdd(a.ctl + kBandX + kLine * x, 1);
+        K = a.gs * (x + a.nxcd * (c / a.gs)) + c % a.gs;
       }
       sm.bcast[0] = K < a.Mb ? K : a.Mb;
     }
@@ -1198,7 +1205,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_sweep(SweepArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[SweepSmem<T>::kBytes];
   __shared__ int ticket;
-  if (threadIdx.x == 0) ticket = atomicAdd(a.ctl + kXTicket + kLine * xcd_id(), 1);
+  if (threadIdx.x == 0) ticket = atomicAdd(a.ctl + kXTicket + kLine * xcd_id(a.nxcd), 1);
   __syncthreads();
   const int tk = ticket;
   if (tk >= 3 && tk < 3 + a.nbxcd) band_worker<T>(a, *reinterpret_cast<BandSmem<T>*>(smem));
@@ -1325,6 +1332,15 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
     return e;
   if (occ < 1) return hipErrorInvalidConfiguration;
   const int grid = ncu * occ;
+  // Bands are dealt to the XCDs, and every XCD needs band workers of its own: take the
+  // device's XCD count (1 when the query is not supported), capped at the slots of the
+  // control area.
+  int nxcd = 1;
+  if (hipDeviceGetAttribute(&nxcd, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || nxcd < 1) {
+    (void)hipGetLastError();
+    nxcd = 1;
+  }
+  a.nxcd = nxcd < kMaxXcd ? nxcd : kMaxXcd;
   // Band workers: enough for the bands that are active at once (a band runs Nj + 3
   // phases, the next one starts about four phases later), at most half the grid.
   int nbw = (a.Nj + 3) / GOUT + 2;
@@ -1333,9 +1349,10 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   if (nbw < 1) nbw = 1;
   // groups of up to eight consecutive bands per XCD, so that every XCD gets bands; one
   // spare band worker per XCD, and a workgroup per XCD left for each task queue
-  a.gs = (a.Mb + NXCD - 1) / NXCD < 8 ? (a.Mb + NXCD - 1) / NXCD : 8;
-  a.nbxcd = (nbw + NXCD - 1) / NXCD + 1;
-  if (a.nbxcd > grid / NXCD - NCLS) a.nbxcd = grid / NXCD - NCLS;
+  const int nx = a.nxcd;
+  a.gs = (a.Mb + nx - 1) / nx < 8 ? (a.Mb + nx - 1) / nx : 8;
+  a.nbxcd = (nbw + nx - 1) / nx + 1;
+  if (a.nbxcd > grid / nx - NCLS) a.nbxcd = grid / nx - NCLS;
   if (a.nbxcd < 1) return hipErrorInvalidConfiguration;
 
   const bool pr = prof_on();
