@@ -116,6 +116,7 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
                     void* workspace, size_t workspace_bytes, int* info, void* stream);
 size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype);
 
+
 /*
  * Three Kronecker factors ("GPTQ-2D: Cubic-Time Two-Sided Adaptive Rounding", arxivlens
  * page, Abstract: the algorithm extends to Hessians with any number of Kronecker
@@ -206,6 +207,15 @@ int gptq2d_gram_accumulate_batched(int count, const int64_t* p, const int64_t* N
  * Returns 0, -1 if n_classes < 0, or GPTQ2D_ERR_HIP if an event query failed.
  */
 int gptq2d_profile_enable(int on);
+/*
+ * The band-update tasks of the window that the last gptq2d_profile_read closed, split by
+ * task class (0 near: 64 deep from the last few bands or column blocks; 1 next: 256 deep,
+ * the first targets of a finished outer band or block; 2 far: 256 deep, the rest): summed
+ * busy time of the workgroups that ran them in CU-milliseconds, task count and dense GEMM
+ * flops, for the first min(n_classes, 3) classes (host arrays, any may be NULL).  Returns 0
+ * or -1 if n_classes < 0.
+ */
+int gptq2d_profile_task_classes(int n_classes, double* cu_ms, int64_t* tasks, double* flops);
 int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* flops,
                         double* bytes);
 const char* gptq2d_profile_class_name(int cls);

@@ -118,15 +118,17 @@ def _wishart_ar1(rng: np.random.Generator, p: int, samples: int, rho: float) -> 
     return a + 0.01 * np.mean(np.diag(a)) * np.eye(p)
 
 
-def _wishart_powerlaw(rng: np.random.Generator, p: int, samples: int, power: float) -> np.ndarray:
-    """X^T X / N with X = Z diag(sqrt(k^-power)) U^T (U Haar), plus 1 % damping."""
+def _wishart_powerlaw(rng: np.random.Generator, p: int, samples: int, power: float,
+                      damp: float = 0.01) -> np.ndarray:
+    """X^T X / N with X = Z diag(sqrt(k^-power)) U^T (U Haar), plus damp (1 %) mean-diagonal
+    damping."""
     u = _haar(rng, p)
     lam = np.arange(1, p + 1, dtype=np.float64) ** (-power)
     z = rng.standard_normal((samples, p))
     x = (z * np.sqrt(lam)[None, :]) @ u.T
     del z, u
     a = _exact_gram(x, 15) / samples
-    return a + 0.01 * np.mean(np.diag(a)) * np.eye(p)
+    return a + damp * np.mean(np.diag(a)) * np.eye(p)
 
 
 def _wishart_iid(rng: np.random.Generator, p: int, samples: int, ridge: float) -> np.ndarray:
@@ -234,7 +236,7 @@ SHAPES = {"C1": (32, 32, 4), "C2": (512, 512, 4), "C3": (4096, 4096, 4),
 # The most recently built large workloads, kept in memory: the transposed 14336-wide layer
 # is built from the untransposed one, and a test process asks for each several times.
 _MEMO: Dict[str, Workload] = {}
-_MEMO_KEEP = 2
+_MEMO_KEEP = 4
 
 
 def _memo_put(name: str, wl: Workload) -> None:
@@ -379,3 +381,16 @@ def make_conditioned(p: int, damp: float, bits: int = 4, seed: int = 0) -> Workl
     return _finish(f"cond{p}d{damp:g}", w, a, b, bits, "f32",
                    f"{p}x{p}; W~N(0,0.02^2); A,B = U diag(k^-1.5) U^T + {damp:g} I (Haar U); "
                    f"{bits}-bit")
+
+
+def make_powerlaw(p: int, power: float, damp: float, bits: int = 4, seed: int = 0) -> Workload:
+    """Square p x p layer with the metrics of the 14336- and 8192-wide layers scaled down: A, B
+    Wishart of p samples with a k^-power spectrum (Haar U) plus damp mean-diagonal damping,
+    W i.i.d. N(0, 0.01^2); the precision study's second family."""
+    gw, ga, gb, _ = _streams(40_000 + seed)
+    w = 0.01 * gw.standard_normal((p, p))
+    a = _wishart_powerlaw(ga, p, p, power, damp)
+    b = _wishart_powerlaw(gb, p, p, power, damp)
+    return _finish(f"pow{p}k{power:g}d{damp:g}", w, a, b, bits, "f32",
+                   f"{p}x{p}; W~N(0,0.01^2); A,B Wishart of {p} samples, spectrum k^-{power:g} "
+                   f"(Haar U) + {damp:g} mean-diagonal damping; {bits}-bit")

@@ -1,0 +1,167 @@
+// Host-side check of the task order of the library's two persistent kernels, built from
+// the same rule header the kernels use (two_sided_adaptive_amd/csrc/schedule.hpp).
+//
+//   factor P0 [P1]    the Cholesky + row inverse of one or two matrices with P0 (and P1)
+//                     tiles per edge, in the kernel's queue order (steps in order, the
+//                     matrices alternating inside a step).  Executes the queue in order and
+//                     checks that every wait of every task is already met by the tasks
+//                     before it, that counter stores never lower a counter, that each task
+//                     appears once, and that every tile of L and X ends final.  A queue
+//                     with that property drains with any number of resident workgroups:
+//                     the earliest unfinished task always has its waits met.
+//   sweep MB NB       the band-update contributions of an MB x NB grid of 64 x 64 blocks:
+//                     per class, direction and target tile, the contributions that the
+//                     blocks publish must carry the ranks 0 .. expected - 1 exactly once,
+//                     in the order of their sources (so each class queue, served in FIFO
+//                     order, never waits for a later task), and the band worker's wait
+//                     targets (expected_class) must equal those counts.
+// Prints one line per check and exits non-zero on the first violation.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <map>
+#include <set>
+#include <tuple>
+#include <vector>
+
+#include "schedule.hpp"
+
+using namespace g2d::sched;
+
+static int fail(const char* what) {
+  fprintf(stderr, "VIOLATION: %s\n", what);
+  return 1;
+}
+
+static int check_factor(const std::vector<int>& ns) {
+  const int nmat = (int)ns.size();
+  int maxn = 0;
+  for (int n : ns) maxn = n > maxn ? n : maxn;
+  std::vector<std::vector<int>> cnt[2];
+  for (int q = 0; q < nmat; ++q) {
+    cnt[q].assign(2, std::vector<int>((size_t)ns[q] * ns[q], 0));
+  }
+  std::set<std::tuple<int, int, int, int, int>> seen;
+  int64_t tasks = 0;
+  char msg[512];
+  for (int g = 0; g < maxn; ++g) {
+    for (int q = 0; q < nmat; ++q) {
+      const int n = ns[q];
+      if (g >= n) continue;
+      const int64_t gsz = group_size(n, g);
+      for (int64_t r = 0; r < gsz; ++r, ++tasks) {
+        const CholTask t = chol_decode(n, g, r);
+        if (t.kind < 0 || t.i < 0 || t.i >= n || t.s < 0 || t.s >= n) {
+          snprintf(msg, sizeof msg, "factor n=%d step %d task %lld decodes out of range", n, g,
+                   (long long)r);
+          return fail(msg);
+        }
+        if (!seen.insert(std::make_tuple(q, t.kind, t.i, t.s, t.j)).second) {
+          snprintf(msg, sizeof msg, "factor n=%d task (%d,%d,%d,%d) listed twice", n, t.kind,
+                   t.i, t.s, t.j);
+          return fail(msg);
+        }
+        CholWait w[4];
+        const int nw = chol_waits(n, t, w);
+        for (int c = 0; c < nw; ++c) {
+          if (w[c].idx < 0 || w[c].idx >= (int64_t)n * n) return fail("wait index out of range");
+          if (cnt[q][w[c].arr][w[c].idx] < w[c].val) {
+            snprintf(msg, sizeof msg,
+                     "factor matrix %d (n=%d) step %d: task kind %d (i=%d s=%d j=%d) waits for "
+                     "counter %d[%lld] >= %d, which only a later task sets (now %d)",
+                     q, n, g, t.kind, t.i, t.s, t.j, w[c].arr, (long long)w[c].idx, w[c].val,
+                     cnt[q][w[c].arr][w[c].idx]);
+            return fail(msg);
+          }
+        }
+        const CholWait sg = chol_signal(n, t);
+        int& v = cnt[q][sg.arr][sg.idx];
+        if (sg.val < v) {
+          snprintf(msg, sizeof msg, "factor n=%d: task kind %d (i=%d s=%d j=%d) lowers a counter",
+                   n, t.kind, t.i, t.s, t.j);
+          return fail(msg);
+        }
+        v = sg.val;
+      }
+    }
+  }
+  for (int q = 0; q < nmat; ++q) {
+    const int n = ns[q];
+    for (int i = 0; i < n; ++i)
+      for (int s = 0; s <= i; ++s) {
+        if (cnt[q][0][(size_t)i * n + s] != kFinal) return fail("a tile of L never became final");
+        if (s < i && cnt[q][1][(size_t)i * n + s] != kFinal)
+          return fail("a tile of X never became final");
+      }
+  }
+  printf("factor");
+  for (int n : ns) printf(" %d", n);
+  printf(": %lld tasks in queue order, every wait met by earlier tasks\n", (long long)tasks);
+  return 0;
+}
+
+static int check_sweep(int Mb, int Nb) {
+  // (class, dir, target band/block, other index) -> ranks seen, by source
+  std::map<std::tuple<int, int, int, int>, std::vector<std::pair<int, int>>> got;
+  int64_t total[NCLS] = {0, 0, 0};
+  for (int K = 0; K < Mb; ++K)
+    for (int L = 0; L < Nb; ++L) {
+      int g0[6], g1[6], np[6];
+      block_groups(K, L, Mb, Nb, g0, g1, np);
+      for (int g = 0; g < 6; ++g) {
+        const int cls = g >> 1, dir = g & 1;
+        const int own = dir == 0 ? K : L, other = dir == 0 ? L : K;
+        for (int k = 0; k < np[g]; ++k) {
+          const int p0 = g0[g] + kPanel * k;
+          const int p1 = p0 + kPanel - 1 < g1[g] ? p0 + kPanel - 1 : g1[g];
+          for (int T = p0; T <= p1; ++T)
+            got[std::make_tuple(cls, dir, T, other)].push_back({own, push_seq(T, own, cls)});
+        }
+        total[cls] += np[g];
+      }
+      for (int c = 0; c < NCLS; ++c)
+        if (np[2 * c] + np[2 * c + 1] != block_task_count(K, L, Mb, Nb, c))
+          return fail("block_task_count differs from the published groups");
+    }
+  char msg[512];
+  for (int cls = 0; cls < NCLS; ++cls)
+    for (int dir = 0; dir < 2; ++dir)
+      for (int T = 0; T < (dir == 0 ? Mb : Nb); ++T)
+        for (int o = 0; o < (dir == 0 ? Nb : Mb); ++o) {
+          const auto it = got.find(std::make_tuple(cls, dir, T, o));
+          const int exp = expected_class(T, cls);
+          const int have = it == got.end() ? 0 : (int)it->second.size();
+          if (have != exp) {
+            snprintf(msg, sizeof msg,
+                     "sweep %dx%d: class %d dir %d target %d (other %d) expects %d contributions, "
+                     "%d are published", Mb, Nb, cls, dir, T, o, exp, have);
+            return fail(msg);
+          }
+          for (int r = 0; r < have; ++r) {
+            const auto& e = it->second[r];  // sources in publication order of one column
+            if (e.second != r) {
+              snprintf(msg, sizeof msg,
+                       "sweep %dx%d: class %d dir %d target %d: source %d has rank %d, expected "
+                       "%d (ranks must follow the sources' order)", Mb, Nb, cls, dir, T, e.first,
+                       e.second, r);
+              return fail(msg);
+            }
+            if (e.first >= T - 1) return fail("a contribution from the band above or later");
+          }
+        }
+  printf("sweep %dx%d: near %lld, next %lld, far %lld tasks; ranks complete and in source order\n",
+         Mb, Nb, (long long)total[0], (long long)total[1], (long long)total[2]);
+  return 0;
+}
+
+int main(int argc, char** argv) {
+  if (argc >= 3 && argv[1][0] == 'f') {
+    std::vector<int> ns;
+    for (int k = 2; k < argc; ++k) ns.push_back(atoi(argv[k]));
+    return check_factor(ns);
+  }
+  if (argc == 4 && argv[1][0] == 's') return check_sweep(atoi(argv[2]), atoi(argv[3]));
+  fprintf(stderr, "usage: %s factor P0 [P1] | sweep MB NB\n", argv[0]);
+  return 2;
+}

@@ -1,0 +1,53 @@
+"""Task order of the two persistent kernels, checked on the host (no GPU).
+
+tests/native/schedule_check.cpp is built from the rule header the kernels themselves
+include (two_sided_adaptive_amd/csrc/schedule.hpp).  For the factor stage it walks the
+queue in order and requires every wait of every task to be met by the tasks before it
+(then the queue drains with any number of resident workgroups: the earliest unfinished
+task can always run); for the sweep it requires the band-update contributions each target
+tile waits for to be published exactly once, with ranks in the order of their sources (so
+every class queue, served first-in first-out, only waits for earlier tasks).  Shapes: the
+five layers (in 64-wide tiles), the odd sizes of the parity tests and a few extremes.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "tests", "native", "schedule_check.cpp")
+INC = os.path.join(ROOT, "two_sided_adaptive_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no C++ compiler")
+    exe = str(tmp_path_factory.mktemp("sched") / "schedule_check")
+    subprocess.run([cxx, "-std=c++17", "-O2", "-Wall", "-Werror", "-I", INC, "-o", exe, SRC],
+                   check=True)
+    return exe
+
+
+def _run(exe, *args):
+    r = subprocess.run([exe, *map(str, args)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr + r.stdout
+    return r.stdout
+
+
+# tiles of 64 per edge: 32 (C1), 512 (C2), 4096 (C3), 14336 / 4096 (C4), 8192 (C5), and the
+# parity tests' odd orders (65, 130, 200, 257, 600, 1030, 1100)
+@pytest.mark.parametrize("tiles", [(1, 1), (8, 8), (64, 64), (224, 64), (64, 224), (128, 128),
+                                   (2, 3), (4, 2), (10, 17), (18,), (5,), (9, 1), (40, 33)])
+def test_factor_queue_never_waits_for_a_later_task(checker, tiles):
+    out = _run(checker, "factor", *tiles)
+    assert "every wait met" in out
+
+
+@pytest.mark.parametrize("blocks", [(64, 64), (224, 64), (64, 224), (128, 128), (1, 1), (1, 7),
+                                    (7, 1), (2, 3), (5, 9), (16, 16), (21, 6), (3, 40)])
+def test_sweep_contributions_complete_and_in_source_order(checker, blocks):
+    out = _run(checker, "sweep", *blocks)
+    assert "ranks complete" in out

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     packed_gemv,
     profile_enable,
     profile_read,
+    profile_task_classes,
     quantize,
     quantize3,
     quantize_factored,

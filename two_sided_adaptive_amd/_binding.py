@@ -57,6 +57,8 @@ _SYMBOLS = {
     "gptq2d_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]),
     "gptq2d_profile_class_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "gptq2d_profile_task_classes": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p,
+                                                   ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 
@@ -319,3 +321,17 @@ def profile_read() -> dict:
     _raise_rc(rc, "gptq2d_profile_read")
     return {lib.gptq2d_profile_class_name(c).decode(): (float(ms[c]), int(la[c]), float(fl[c]),
                                                          float(by[c])) for c in range(n)}
+
+
+def profile_task_classes() -> dict:
+    """Band-update tasks of the last profile_read window by task class:
+    {"near"|"next"|"far": (busy CU-ms, tasks, flops)}."""
+    import numpy as np
+    lib = load_library()
+    ms = np.zeros(3)
+    n = np.zeros(3, dtype=np.int64)
+    fl = np.zeros(3)
+    _raise_rc(lib.gptq2d_profile_task_classes(3, ms.ctypes.data, n.ctypes.data, fl.ctypes.data),
+              "gptq2d_profile_task_classes")
+    return {name: (float(ms[c]), int(n[c]), float(fl[c]))
+            for c, name in enumerate(("near", "next", "far"))}

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["api.hip", "factor.hip", "sweep.hip", "kron3.hip", "pack.hip", "gram.hip"]
-HEADERS = ["common.hpp", "launch.hpp", "prof.hpp"]
+HEADERS = ["common.hpp", "launch.hpp", "prof.hpp", "schedule.hpp"]
 LIB = os.path.join(PKG, "libgptq2d.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

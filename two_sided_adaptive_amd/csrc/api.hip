@@ -31,6 +31,9 @@ struct ProfState {
   hipEvent_t open[KC_COUNT] = {};
   double ms[KC_COUNT] = {}, flops[KC_COUNT] = {}, bytes[KC_COUNT] = {};
   int64_t launches[KC_COUNT] = {};
+  // band-update tasks per task class (near, next, far) in the window of the last read
+  double last_task_ms[kTaskClasses] = {}, last_task_flops[kTaskClasses] = {};
+  int64_t last_task_n[kTaskClasses] = {};
   hipEvent_t get() {
     if (!pool.empty()) {
       hipEvent_t e = pool.back();
@@ -118,6 +121,26 @@ int clear_info(int* info, hipStream_t s) {
 }
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : GPTQ2D_ERR_HIP; }
+
+// Factor A and B (one persistent launch), then the sweep, on stream s, with the workspace
+// at ws (at least gptq2d_workspace_bytes(m, n, dtype) bytes, 256-byte aligned).
+int quantize_enqueue(int64_t m, int64_t n, int bits, int dtype, const void* W, const void* A,
+                     const void* B, const void* scales, int8_t* codes, void* Q, void* ws,
+                     int* info, hipStream_t s) {
+  const size_t es = dtype == GPTQ2D_F32 ? sizeof(float) : sizeof(double);
+  char* c = (char*)ws;
+  void* Ua = c;
+  c += align_up((size_t)m * m * es);
+  void* Ub = c;
+  c += align_up((size_t)n * n * es);
+  void* scratch_a = c;
+  void* scratch_b = c + g2d::factor_workspace(m);
+  hipError_t e =
+      g2d::factor_pair_enqueue(m, A, Ua, scratch_a, n, B, Ub, scratch_b, dtype, info, s);
+  if (e == hipSuccess)
+    e = g2d::sweep_enqueue(m, n, bits, dtype, W, Ua, Ub, scales, codes, Q, c, info, s);
+  return status(e);
+}
 
 }  // namespace
 
@@ -207,21 +230,10 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
   int rc = ws.acquire(workspace, workspace_bytes, need, s);
   if (rc) return rc;
   if ((rc = clear_info(info, s))) return rc;
-  const size_t es = dtype == GPTQ2D_F32 ? sizeof(float) : sizeof(double);
-  char* c = (char*)ws.ptr;
-  void* Ua = c;
-  c += align_up((size_t)m * m * es);
-  void* Ub = c;
-  c += align_up((size_t)n * n * es);
-  void* scratch = c;
-  void* scratch_b = c + g2d::factor_workspace(m);
   // Both factors in one persistent launch, then the sweep, on the caller's stream.
-  hipError_t e =
-      g2d::factor_pair_enqueue(m, A, Ua, scratch, n, B, Ub, scratch_b, dtype, info, s);
-  if (e == hipSuccess)
-    e = g2d::sweep_enqueue(m, n, bits, dtype, W, Ua, Ub, scales, codes, Q, scratch, info, s);
-  return status(e);
+  return quantize_enqueue(m, n, bits, dtype, W, A, B, scales, codes, Q, ws.ptr, info, s);
 }
+
 
 size_t gptq2d_workspace3_bytes(int64_t m1, int64_t m2, int64_t m3, int dtype) {
   if (m1 <= 0 || m2 <= 0 || m3 <= 0 || m1 > kMaxDim || m2 > kMaxDim || m3 > kMaxDim ||
@@ -362,12 +374,17 @@ int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* fl
   }
   p.pending.clear();
   {
-    double cu_ms = 0.0, fl = 0.0;
-    int64_t tasks = 0;
-    if (g2d::band_stats_collect(&cu_ms, &fl, &tasks) != hipSuccess) rc = GPTQ2D_ERR_HIP;
-    p.ms[g2d::KC_BAND_GEMM] += cu_ms;
-    p.flops[g2d::KC_BAND_GEMM] += fl;
-    p.launches[g2d::KC_BAND_GEMM] += tasks;
+    double cu_ms[g2d::kTaskClasses] = {}, fl[g2d::kTaskClasses] = {};
+    int64_t tasks[g2d::kTaskClasses] = {};
+    if (g2d::band_stats_collect(cu_ms, fl, tasks) != hipSuccess) rc = GPTQ2D_ERR_HIP;
+    for (int c = 0; c < g2d::kTaskClasses; ++c) {
+      p.ms[g2d::KC_BAND_GEMM] += cu_ms[c];
+      p.flops[g2d::KC_BAND_GEMM] += fl[c];
+      p.launches[g2d::KC_BAND_GEMM] += tasks[c];
+      p.last_task_ms[c] = cu_ms[c];
+      p.last_task_flops[c] = fl[c];
+      p.last_task_n[c] = tasks[c];
+    }
   }
   const int n = n_classes < g2d::KC_COUNT ? n_classes : g2d::KC_COUNT;
   for (int c = 0; c < n; ++c) {
@@ -381,6 +398,19 @@ int gptq2d_profile_read(int n_classes, double* ms, int64_t* launches, double* fl
     p.launches[c] = 0;
   }
   return rc;
+}
+
+int gptq2d_profile_task_classes(int n_classes, double* cu_ms, int64_t* tasks, double* flops) {
+  if (n_classes < 0) return -1;
+  g2d::ProfState& p = g2d::prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  const int n = n_classes < g2d::kTaskClasses ? n_classes : g2d::kTaskClasses;
+  for (int c = 0; c < n; ++c) {
+    if (cu_ms) cu_ms[c] = p.last_task_ms[c];
+    if (tasks) tasks[c] = p.last_task_n[c];
+    if (flops) flops[c] = p.last_task_flops[c];
+  }
+  return 0;
 }
 
 const char* gptq2d_profile_class_name(int cls) {

@@ -19,6 +19,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "prof.hpp"
+#include "schedule.hpp"
 
 namespace g2d {
 namespace {
@@ -619,9 +620,7 @@ __device__ inline void chol_xchunk(int64_t p, int i, int s, int klo, int khi, bo
 // Group (q, g) lists bulk(g) of column g + 1 first, then crit(g), then the rest of
 // bulk(g) column by column, then xrow(g) by jj and s; groups go by step, the matrices
 // alternating.  Every task depends only on earlier tasks, so the queue always drains.
-constexpr int kInvDepth = 8;   // tiles of k per chunk of the row inverse
-constexpr int kInvFirst = 8;   // tiles of k of a row's last chunk
-constexpr int kInvStride = 2;  // steps between the chunks of one row (<= kInvFirst + 1)
+using namespace sched;  // task order, waits and signals (schedule.hpp)
 constexpr int kMaxChol = 2;
 struct CholMat {
   int64_t p;
@@ -645,32 +644,6 @@ struct CholArgs {
   int* info;
 };
 constexpr int kCholSpin = 1 << 20;
-constexpr int kFinal = 1 << 24;  // tile counter of a final tile
-
-// Tasks in group (q, g) of the Cholesky: n - g - 1 + n - g + (n - g - 2)(n - g - 1) / 2
-// = u (u + 1) / 2 with u = n - g for g >= 1, and n for g = 0 (panel steps only).
-__host__ __device__ inline int64_t chol_group_size(int n, int g) {
-  const int64_t u = n - g;
-  return g == 0 ? n : u * (u + 1) / 2;
-}
-// xrow tasks of chunk jj in group g (row i = g + kInvStride jj): chunk 0 of every s < g;
-// for jj >= 1 the columns s < khi = g - (kInvDepth - kInvStride) jj + kInvDepth - kInvFirst
-// (a count that falls with jj).
-__host__ __device__ inline int xrow_count(int n, int g, int jj) {
-  if (g + kInvStride * jj >= n) return 0;
-  if (jj == 0) return g;
-  const int cnt = g - (kInvDepth - kInvStride) * jj + kInvDepth - kInvFirst;
-  return cnt > 0 ? cnt : 0;
-}
-__host__ __device__ inline int64_t group_size(int n, int g) {
-  int64_t c = chol_group_size(n, g) + xrow_count(n, g, 0);
-  for (int jj = 1; xrow_count(n, g, jj) > 0; ++jj) c += xrow_count(n, g, jj);
-  return c;
-}
-// chunks of the row inverse of tile (i, s), i > s
-__host__ __device__ inline int xrow_chunks(int i, int s) {
-  return 1 + (i - s > kInvFirst ? (i - s - kInvFirst + kInvDepth - 1) / kInvDepth : 0);
-}
 
 // Clears the control words and tile counters of up to two matrices and writes each
 // matrix's task table tab[g] = tasks of the matrix before step g (n + 1 entries).  One
@@ -782,43 +755,10 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
           r -= sz0;
           q = 1;
         }
-        const int n = q == 0 ? n0 : n1;
-        int k = (int)r;
-        const int c1 = g >= 1 ? n - g - 1 : 0, c2 = n - g;
-        const int64_t cg = chol_group_size(n, g);
-        if (k < c1) {
-          kind = 0;
-          i = g + 1 + k;
-          x = (g << 16) | (g + 1);
-        } else if (k < c1 + c2) {
-          kind = 1;
-          i = g + (k - c1);
-          x = g << 16;
-        } else if (k < cg) {
-          kind = 0;
-          k -= c1 + c2;
-          int j = g + 2;
-          while (k >= n - j && j < n) {
-            k -= n - j;
-            ++j;
-          }
-          i = j + k;
-          x = (g << 16) | j;
-        } else {
-          kind = 2;
-          k -= (int)cg;
-          int jj = 0;
-          if (k >= xrow_count(n, g, 0)) {
-            k -= xrow_count(n, g, 0);
-            jj = 1;
-            while (jj < n && k >= xrow_count(n, g, jj)) {  // (k < the group's xrow tasks)
-              k -= xrow_count(n, g, jj);
-              ++jj;
-            }
-          }
-          i = g + kInvStride * jj;
-          x = (k << 16) | jj;  // s = k
-        }
+        const CholTask ct = chol_decode(q == 0 ? n0 : n1, g, r);
+        kind = ct.kind;
+        i = ct.i;
+        x = (ct.s << 16) | ct.j;
       }
       if (lane == 0) {
         task[0] = kind;
@@ -840,39 +780,22 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
     const CholMat m = q == 0 ? a.mat[0] : a.mat[1];
     const int64_t p = m.p;
     const int n = m.nblk;
+    const CholTask ct{kind, i, s, j};
     // kind 2: chunk j of tile (i, s) covers k in [klo, khi)
-    const int khi = j == 0 ? i : i - kInvFirst - kInvDepth * (j - 1), nch = xrow_chunks(i, s);
-    const int klo0 = khi - (j == 0 ? kInvFirst : kInvDepth), klo = klo0 > s ? klo0 : s;
-    // dependencies (wave 0 waits, the barrier releases the others)
+    int klo = 0, khi = 0;
+    xrow_range(ct, &klo, &khi);
+    const int nch = xrow_chunks(i, s);
+    // dependencies (wave 0 waits, the barrier releases the others); every task polls only
+    // the few tiles it reads, so the waiters of one step spread over many words
     if (w == 0) {
-      // every task polls only the few tiles it reads, so the waiters of one step spread
-      // over many words
-      const int* tc = m.tile_cnt;
+      CholWait cw[4];
+      const int nw = chol_waits(n, ct, cw);
       bool ok = true;
-      if (kind == 2) {
-        // L_i,khi-1 final (so every L_ik, k < khi), X_khi-1,s final (so every X_ks,
-        // s <= k < khi), the previous chunks of this tile, and X_ii for the last chunk
-        ok = chol_wait(tc + (int64_t)i * n + (khi - 1), kFinal, a.ctl, a.info);
-        if (ok)
-          ok = chol_wait(khi - 1 == s ? tc + (int64_t)s * n + s : m.xcnt + (int64_t)(khi - 1) * n + s,
-                         kFinal, a.ctl, a.info);
-        if (ok && j < nch - 1)
-          ok = chol_wait(m.xcnt + (int64_t)i * n + s, nch - 1 - j, a.ctl, a.info);
-        if (ok && j == 0) ok = chol_wait(tc + (int64_t)i * n + i, kFinal, a.ctl, a.info);
-      } else {
-        // the panel tiles this task reads are final (kFinal), and its own tiles carry
-        // panels 0 .. s - 2
-        const int r2 = kind == 0 ? j : s;  // the second panel row read
-        if (s >= 1) {
-          ok = chol_wait(tc + (int64_t)i * n + (s - 1), kFinal, a.ctl, a.info);
-          if (ok && r2 != i) ok = chol_wait(tc + (int64_t)r2 * n + (s - 1), kFinal, a.ctl, a.info);
-        }
-        if (ok && kind == 0) ok = chol_wait(tc + (int64_t)i * n + j, s - 1, a.ctl, a.info);
-        if (ok && kind == 1 && s >= 2) {
-          ok = chol_wait(tc + (int64_t)s * n + s, s - 1, a.ctl, a.info);
-          if (ok && i != s) ok = chol_wait(tc + (int64_t)i * n + s, s - 1, a.ctl, a.info);
-        }
-      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (ok && c < nw)
+          ok = chol_wait((cw[c].arr == 0 ? m.tile_cnt : m.xcnt) + cw[c].idx, cw[c].val, a.ctl,
+                         a.info);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __syncthreads();
@@ -895,12 +818,9 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (w == 0 && lane == 0) {
-      if (kind == 2)
-        __hip_atomic_store(m.xcnt + (int64_t)i * n + s, j == 0 ? kFinal : nch - j,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else
-        __hip_atomic_store(m.tile_cnt + (int64_t)i * n + (kind == 0 ? j : s),
-                           kind == 0 ? s : kFinal, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const CholWait sg = chol_signal(n, ct);
+      __hip_atomic_store((sg.arr == 0 ? m.tile_cnt : m.xcnt) + sg.idx, sg.val, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

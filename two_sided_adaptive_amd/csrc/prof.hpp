@@ -25,10 +25,12 @@ void prof_begin(int cls, hipStream_t s);
 void prof_end(int cls, hipStream_t s, double flops, double bytes);
 
 // Device counters of the band-update tasks, accumulated by the sweep kernel while the
-// hook is on (nullptr otherwise): [0] busy wall-clock ticks (100 MHz) summed over tasks,
-// [1] task flops, [2] tasks.
+// hook is on (nullptr otherwise), per task class c (near, next, far):
+// [3c] busy wall-clock ticks (100 MHz) summed over tasks, [3c + 1] task flops, [3c + 2] tasks.
+constexpr int kTaskClasses = 3;
 unsigned long long* band_stats_device();
-// Reads the counters into the class totals and clears them (synchronous).
+// Reads the counters of each task class (arrays of kTaskClasses) and clears them
+// (synchronous).
 hipError_t band_stats_collect(double* cu_ms, double* flops, int64_t* tasks);
 
 }  // namespace g2d

@@ -39,6 +39,8 @@
 //     the order of their sources, so the result is deterministic.
 // Every wait is bounded; a timeout aborts the sweep and reports info[0] = 4.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include <mutex>
 #include <vector>
@@ -46,17 +48,15 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "prof.hpp"
+#include "schedule.hpp"
 
 namespace g2d {
 namespace {
 
+using namespace sched;  // task rules shared with the host-side schedule checker
+
 constexpr int BB = 64;      // band height = block edge
 constexpr int MU = 16;      // micro-tile edge
-constexpr int GOUT = 4;     // bands (blocks) per outer band (block)
-// far pushes of outer band (block) O reach targets >= GOUT (O + 1) + FAR_OFF; with an
-// offset of 2 a 256-deep task has a few phases to finish before its target needs it
-constexpr int FAR_OFF = 2;
-constexpr int kPanel = 2;   // target blocks per GEMM task
 constexpr int kThreads = 256;
 constexpr int kSpinLimit = 1 << 22;
 // accelerator complex dies (XCDs), one L2 each: 8 on an MI355X in its default partition
@@ -74,16 +74,7 @@ enum Ctl : int {
   kXTicket = kLine * (7 + kMaxXcd),    // + kLine x: workgroups started on XCD x
   kCtlWords = kLine * (7 + 2 * kMaxXcd)
 };
-// Band-update contributions come in three classes, each with its own accumulators,
-// contribution counters, task queue and workers:
-//   near: 64 deep, from the last few bands / blocks before the target;
-//   next: 256 deep, from the last outer band / block to the first kPanel targets it
-//         reaches (the far contribution that is needed soonest after it is published);
-//   far:  256 deep, every other contribution of whole outer bands / blocks.
-// A contribution only ever waits for earlier contributions of its own class, so each
-// queue is served in FIFO order, and urgent tasks never wait behind the backlog of far
-// ones.
-enum PushClass : int { kNear = 0, kNext = 1, kFar = 2, NCLS = 3 };
+// (band-update classes near / next / far: schedule.hpp)
 
 // Cache policy of loads and stores that other workgroups of the same launch produce or
 // consume: device scope (sc1), so they bypass the non-coherent caches.
@@ -115,66 +106,6 @@ struct SweepArgs {
   unsigned long long* qd[NCLS]; // [qcap] per class: task descriptors (0 = not yet published)
   unsigned long long* stats; // band-update task accounting while profiling, else null
 };
-
-// ---------------------------------------------------------------------------
-// push rules (host and device)
-// ---------------------------------------------------------------------------
-// Source index `own` (a band for vertical pushes, a column block for horizontal ones)
-// pushes 64 deep to targets [own + 2, GOUT (own / GOUT) + GOUT - 1 + FAR_OFF]; the last
-// band of an outer band pushes the whole outer band, 256 deep, to every target from
-// GOUT (own / GOUT + 1) + FAR_OFF on (FAR_OFF >= 1).  Target T thus receives, in
-// source order, the far pushes of outer bands 0 .. nfar(T) - 1 and then the near pushes
-// of the bands GOUT nfar(T) .. T - 2; band T - 1 is applied by the band worker itself.
-__host__ __device__ inline int nfar(int T) {
-  return T >= GOUT + FAR_OFF ? (T - GOUT - FAR_OFF) / GOUT + 1 : 0;
-}
-// T is among the first kPanel targets of the far range of outer band nfar(T) - 1, whose
-// push to T is then of class kNext
-__host__ __device__ inline bool next_push(int T) {
-  return T >= GOUT + FAR_OFF && (T - GOUT - FAR_OFF) % GOUT < kPanel;
-}
-// contributions of one class that target T receives, and a contribution's rank in them
-__host__ __device__ inline int expected_class(int T, int cls) {
-  const int nf = nfar(T), nx = next_push(T) ? 1 : 0;
-  if (cls == kNear) return T >= 2 ? T - 1 - GOUT * nf : 0;
-  return cls == kNext ? nx : nf - nx;
-}
-__host__ __device__ inline int push_seq(int T, int own, int cls) {
-  if (cls == kNear) return own - GOUT * nfar(T);
-  return cls == kNext ? 0 : own / GOUT;
-}
-__host__ __device__ inline void near_range(int own, int nt, int* t0, int* t1) {
-  *t0 = own + 2;
-  const int e = GOUT * (own / GOUT) + GOUT - 1 + FAR_OFF;
-  *t1 = e < nt - 1 ? e : nt - 1;
-}
-__host__ __device__ inline void far_range(int own, int nt, int* t0, int* t1) {
-  if (own % GOUT != GOUT - 1) {
-    *t0 = 1;
-    *t1 = 0;
-    return;
-  }
-  *t0 = GOUT * (own / GOUT + 1) + FAR_OFF;
-  *t1 = nt - 1;
-}
-__host__ __device__ inline int npanels(int t0, int t1) {
-  return t1 >= t0 ? (t1 - t0) / kPanel + 1 : 0;
-}
-__host__ __device__ inline int block_task_count(int K, int L, int Mb, int Nb, int cls) {
-  int t0, t1, c = 0;
-  for (int dir = 0; dir < 2; ++dir) {
-    const int own = dir == 0 ? K : L, nt = dir == 0 ? Mb : Nb;
-    if (cls == kNear) {
-      near_range(own, nt, &t0, &t1);
-      c += npanels(t0, t1);
-    } else {
-      far_range(own, nt, &t0, &t1);
-      const int np = npanels(t0, t1);  // the first panel is the kNext task
-      c += cls == kNext ? (np > 0 ? 1 : 0) : (np > 0 ? np - 1 : 0);
-    }
-  }
-  return c;
-}
 
 // descriptor: bit 63 valid | 62 far | 61 horizontal | [45,60) own | [30,45) other |
 // [15,30) last target | [0,15) first target
@@ -770,22 +701,7 @@ template <typename T>
 __device__ inline void publish_block(const SweepArgs<T>& a, int K, int L, int base, int lane) {
   // six groups (class, direction): first target, last target, panel count
   int g0[6], g1[6], np[6];
-  for (int dir = 0; dir < 2; ++dir) {
-    const int own = dir == 0 ? K : L, nt = dir == 0 ? a.Mb : a.Nb;
-    int t0, t1;
-    near_range(own, nt, &t0, &t1);
-    g0[2 * kNear + dir] = t0;
-    g1[2 * kNear + dir] = t1;
-    np[2 * kNear + dir] = npanels(t0, t1);
-    far_range(own, nt, &t0, &t1);
-    const int nf = npanels(t0, t1);
-    g0[2 * kNext + dir] = t0;
-    g1[2 * kNext + dir] = t0 + kPanel - 1 < t1 ? t0 + kPanel - 1 : t1;
-    np[2 * kNext + dir] = nf > 0 ? 1 : 0;
-    g0[2 * kFar + dir] = t0 + kPanel;
-    g1[2 * kFar + dir] = t1;
-    np[2 * kFar + dir] = nf > 0 ? nf - 1 : 0;
-  }
+  block_groups(K, L, a.Mb, a.Nb, g0, g1, np);
   int total = 0;
 #pragma unroll
   for (int g = 0; g < 6; ++g) total += np[g];
@@ -1182,9 +1098,10 @@ __device__ __attribute__((always_inline)) inline void gemm_worker(const SweepArg
         st_dev(cnt, push_seq(t, own, cls) + 1);
       }
       if (a.stats) {
-        atomicAdd(a.stats + 0, (unsigned long long)(wall_clock64() - t_begin));
-        atomicAdd(a.stats + 1, (unsigned long long)(2 * (int64_t)PW * QW * ks));
-        atomicAdd(a.stats + 2, 1ull);
+        unsigned long long* st = a.stats + 3 * cls;
+        atomicAdd(st + 0, (unsigned long long)(wall_clock64() - t_begin));
+        atomicAdd(st + 1, (unsigned long long)(2 * (int64_t)PW * QW * ks));
+        atomicAdd(st + 2, 1ull);
       }
     }
   }
@@ -1275,8 +1192,71 @@ SyncLayout sync_layout(int64_t m, int64_t n) {
   return s;
 }
 
+// How many band workers each XCD gets (b) and how many consecutive bands go to one XCD
+// (gs).  The sweep takes about max(pipeline, updates): the band pipeline's phases, from a
+// simulation of the dealing (band K starts four phases after band K - 1 and once a band
+// worker of its XCD is free; a band takes Nj + 3 phases), times a phase's duration, against
+// the band updates' flops over the rate of the CUs left to them.  Both rates were measured
+// on the 4096-wide layer: a phase takes 12.9 us (fp64) or 9.3 us (fp32), a CU running
+// update tasks sustains 0.175 (fp64) or 0.276 (fp32) TFLOP/s, 80 % of the time busy.  The
+// default (b0, gs0) keeps every band of the pipeline active at once and is kept unless
+// another plan is estimated at least 10 % faster.  GPTQ2D_SWEEP_BANDS="b,gs" overrides the
+// plan (a tuning knob; values are clamped to what the grid allows).
+struct BandPlan {
+  int b, gs;
+};
+double pipeline_phases(int Mb, int Nj, int nx, int b, int gs) {
+  std::vector<double> free_at((size_t)nx * b, 0.0);
+  double prev = -(double)GOUT, end = 0.0;
+  for (int K = 0; K < Mb; ++K) {
+    const int x = (K / gs) % nx;
+    double* f = &free_at[(size_t)x * b];
+    int w = 0;
+    for (int i = 1; i < b; ++i)
+      if (f[i] < f[w]) w = i;
+    const double st = prev + GOUT > f[w] ? prev + GOUT : f[w];
+    f[w] = st + Nj + 3;
+    prev = st;
+    if (f[w] > end) end = f[w];
+  }
+  return end;
+}
+BandPlan plan_bands(int64_t m, int64_t n, int Mb, int Nj, int nx, int grid, int b0, int gs0,
+                    bool f64) {
+  const int bmax = grid / nx - NCLS;
+  BandPlan best{b0, gs0};
+  if (const char* env = getenv("GPTQ2D_SWEEP_BANDS")) {
+    int b = 0, gs = 0;
+    if (sscanf(env, "%d,%d", &b, &gs) == 2 && b >= 1 && gs >= 1) {
+      best.b = b < bmax ? b : bmax;
+      best.gs = gs;
+      return best;
+    }
+  }
+  const double phase = f64 ? 12.9e-6 : 9.3e-6;
+  const double rate = (f64 ? 0.175e12 : 0.276e12) * 0.8;
+  const double flops = 0.96 * (double)m * (double)n * (double)(m + n);
+  auto est = [&](int b, int gs) {
+    const double tp = pipeline_phases(Mb, Nj, nx, b, gs) * phase;
+    const double tg = flops / (rate * (double)(grid - nx * b));
+    return tp > tg ? tp : tg;
+  };
+  const double t0 = est(b0, gs0);
+  double tb = t0;
+  for (int gs = gs0; gs >= 1; gs /= 2)
+    for (int b = b0; b >= 1; --b) {
+      const double t = est(b, gs);
+      if (t < tb) {
+        tb = t;
+        best = BandPlan{b, gs};
+      }
+    }
+  if (tb > 0.9 * t0) best = BandPlan{b0, gs0};
+  return best;
+}
+
 // band-update task accounting of the measurement hook (see prof.hpp)
-__device__ unsigned long long g_band_stats[3];
+__device__ unsigned long long g_band_stats[3 * NCLS];
 
 template <typename T>
 hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, const T* Ub,
@@ -1342,17 +1322,21 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   }
   a.nxcd = nxcd < kMaxXcd ? nxcd : kMaxXcd;
   // Band workers: enough for the bands that are active at once (a band runs Nj + 3
-  // phases, the next one starts about four phases later), at most half the grid.
+  // phases, the next one starts about four phases later), at most half the grid; groups
+  // of up to eight consecutive bands per XCD, one spare band worker per XCD, and a
+  // workgroup per XCD left for each task queue.  On layers whose band updates outweigh the
+  // pipeline, fewer band workers leave more CUs to the updates (plan_bands).
   int nbw = (a.Nj + 3) / GOUT + 2;
   if (nbw > a.Mb) nbw = a.Mb;
   if (nbw > grid / 2) nbw = grid / 2;
   if (nbw < 1) nbw = 1;
-  // groups of up to eight consecutive bands per XCD, so that every XCD gets bands; one
-  // spare band worker per XCD, and a workgroup per XCD left for each task queue
   const int nx = a.nxcd;
-  a.gs = (a.Mb + nx - 1) / nx < 8 ? (a.Mb + nx - 1) / nx : 8;
-  a.nbxcd = (nbw + nx - 1) / nx + 1;
-  if (a.nbxcd > grid / nx - NCLS) a.nbxcd = grid / nx - NCLS;
+  const int gs0 = (a.Mb + nx - 1) / nx < 8 ? (a.Mb + nx - 1) / nx : 8;
+  int b0 = (nbw + nx - 1) / nx + 1;
+  if (b0 > grid / nx - NCLS) b0 = grid / nx - NCLS;
+  const BandPlan bp = plan_bands(m, n, a.Mb, a.Nj, nx, grid, b0, gs0, sizeof(T) == 8);
+  a.gs = bp.gs;
+  a.nbxcd = bp.b;
   if (a.nbxcd < 1) return hipErrorInvalidConfiguration;
 
   const bool pr = prof_on();
@@ -1390,15 +1374,17 @@ unsigned long long* band_stats_device() {
 }
 
 hipError_t band_stats_collect(double* cu_ms, double* flops, int64_t* tasks) {
-  unsigned long long h[3] = {0, 0, 0};
+  unsigned long long h[3 * NCLS] = {};
   hipError_t e = hipMemcpyFromSymbol(h, HIP_SYMBOL(g_band_stats), sizeof(h), 0,
                                      hipMemcpyDeviceToHost);
   if (e != hipSuccess) return e;
-  const unsigned long long z[3] = {0, 0, 0};
+  const unsigned long long z[3 * NCLS] = {};
   e = hipMemcpyToSymbol(HIP_SYMBOL(g_band_stats), z, sizeof(z), 0, hipMemcpyHostToDevice);
-  *cu_ms = (double)h[0] * 1e-5;  // 100 MHz ticks -> ms
-  *flops = (double)h[1];
-  *tasks = (int64_t)h[2];
+  for (int c = 0; c < NCLS; ++c) {
+    cu_ms[c] = (double)h[3 * c] * 1e-5;  // 100 MHz ticks -> ms
+    flops[c] = (double)h[3 * c + 1];
+    tasks[c] = (int64_t)h[3 * c + 2];
+  }
   return e;
 }
 
