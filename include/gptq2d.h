@@ -63,6 +63,10 @@ extern "C" {
 
 #define GPTQ2D_ERR_HIP 1          /* a HIP runtime call failed */
 #define GPTQ2D_ERR_ALLOC 2        /* device allocation failed */
+#define GPTQ2D_ERR_SCRATCH 3      /* problem too large for gptq2d_quantize_noalloc's buffer */
+
+/* Size of the static per-device scratch buffer of gptq2d_quantize_noalloc (64 MiB). */
+#define GPTQ2D_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
 /*
  * Factor stage: the unit upper triangular feedback factor of one SPD matrix.
@@ -116,6 +120,25 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
                     void* workspace, size_t workspace_bytes, int* info, void* stream);
 size_t gptq2d_workspace_bytes(int64_t m, int64_t n, int dtype);
 
+/*
+ * gptq2d_quantize for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * semantics and results as gptq2d_quantize, minus the workspace: the library uses a static
+ * scratch buffer of GPTQ2D_NOALLOC_SCRATCH_BYTES in each device's memory (reserved when
+ * the library's code is first loaded on a device and held until the process ends) and
+ * calls no allocating routine (hipMalloc, hipMallocAsync, hipFree, torch).
+ *   Limit: problems with gptq2d_workspace_bytes(m, n, dtype) > GPTQ2D_NOALLOC_SCRATCH_BYTES
+ *   return GPTQ2D_ERR_SCRATCH before any HIP call (m = n = 896 in F64 and m = n = 1024 in
+ *   F32 fit).
+ *   All calls on one device share that device's buffer: calls that overlap in time on one
+ *   device (two streams, two threads) race on it and their outputs are undefined.  The
+ *   buffer keeps the last call's contents; the kernels clear or overwrite everything they
+ *   read before reading it.
+ *   args: m, n, bits, dtype, W, A, B, scales, codes, Q, info, stream (as gptq2d_quantize)
+ */
+int gptq2d_quantize_noalloc(int64_t m, int64_t n, int bits, int dtype, const void* W,
+                            const void* A, const void* B, const void* scales, int8_t* codes,
+                            void* Q, int* info, void* stream);
 
 /*
  * Three Kronecker factors ("GPTQ-2D: Cubic-Time Two-Sided Adaptive Rounding", arxivlens

@@ -138,3 +138,24 @@ def test_gram_arguments_rejected_on_host(lib):
     P[1] = 4
     assert lib.gptq2d_gram_accumulate_batched(2, P, N, 7, X, al, X, None) == -4
     assert lib.gptq2d_gram_accumulate_batched(2, P, N, 1, None, al, X, None) == -5
+
+
+def test_noalloc_arguments_and_limit_checked_on_host(lib):
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    q = lib.gptq2d_quantize_noalloc
+    ok = [4, 4, 4, 1, p, p, p, p, p, p, None, None]
+    for i, bad in [(0, 0), (1, -2), (2, 1), (2, 9), (3, 2)]:
+        args = list(ok)
+        args[i] = bad
+        assert q(*args) == -(i + 1), (i, bad)
+    for i in range(4, 10):  # null W, A, B, scales, codes, Q
+        args = list(ok)
+        args[i] = None
+        assert q(*args) == -(i + 1), i
+    # a problem whose workspace exceeds the static buffer is refused before any HIP call
+    limit = 64 << 20
+    assert lib.gptq2d_workspace_bytes(896, 896, 1) <= limit
+    assert lib.gptq2d_workspace_bytes(1024, 1024, 1) > limit
+    assert q(1024, 1024, 4, 1, p, p, p, p, p, p, None, None) == 3
+    assert q(2000, 64, 4, 0, p, p, p, p, p, p, None, None) == 3
+    assert b"scratch" in lib.gptq2d_strerror(3)

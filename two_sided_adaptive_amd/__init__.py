@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     quantize,
     quantize3,
     quantize_factored,
+    quantize_noalloc,
     unpack,
     workspace_bytes,
 )

@@ -32,6 +32,9 @@ _SYMBOLS = {
                                        ctypes.c_int] + [ctypes.c_void_p] * 6 +
                         [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "gptq2d_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
+    "gptq2d_quantize_noalloc": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.c_int] + [ctypes.c_void_p] * 6 +
+                                [ctypes.c_void_p, ctypes.c_void_p]),
     "gptq2d_quantize3": (ctypes.c_int, [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_int] +
                          [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_size_t,
                                                   ctypes.c_void_p, ctypes.c_void_p]),
@@ -198,6 +201,29 @@ def quantize(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, bits: int, scale
     if check:
         _check_info(info)
     return codes, Q
+
+
+def quantize_noalloc(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, bits: int,
+                     scales: torch.Tensor, out: Tuple[torch.Tensor, torch.Tensor],
+                     info: Optional[torch.Tensor] = None) -> None:
+    """gptq2d_quantize_noalloc: the whole call into caller-provided (codes, Q), with the
+    library's static scratch buffer instead of a workspace.  Allocates nothing: `info`
+    (device int32[2]) is optional and is not read back here."""
+    lib = load_library()
+    m, n = W.shape
+    dt = _dt(W)
+    _check_dev("W", W, W.dtype, (m, n))
+    _check_dev("A", A, W.dtype, (m, m))
+    _check_dev("B", B, W.dtype, (n, n))
+    _check_dev("scales", scales, W.dtype, (m,))
+    codes, Q = out
+    _check_dev("codes", codes, torch.int8, (m, n))
+    _check_dev("Q", Q, W.dtype, (m, n))
+    rc = lib.gptq2d_quantize_noalloc(m, n, int(bits), dt, W.data_ptr(), A.data_ptr(),
+                                     B.data_ptr(), scales.data_ptr(), codes.data_ptr(),
+                                     Q.data_ptr(), info.data_ptr() if info is not None else None,
+                                     _stream(W.device))
+    _raise_rc(rc, "gptq2d_quantize_noalloc")
 
 
 def quantize3(W: torch.Tensor, A1: torch.Tensor, A2: torch.Tensor, A3: torch.Tensor, bits: int,

@@ -142,6 +142,38 @@ int quantize_enqueue(int64_t m, int64_t n, int bits, int dtype, const void* W, c
   return status(e);
 }
 
+// ---------------------------------------------------------------------------
+// static scratch of gptq2d_quantize_noalloc
+// ---------------------------------------------------------------------------
+// One buffer per device, in the code object's device memory: it exists on every device the
+// library runs on until the process ends, and the entry point never allocates.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device address is
+// looked up once per device (scratch_address) and only that address is used.
+constexpr size_t kNoAllocBytes = (size_t)GPTQ2D_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of this device's scratch buffer (looked up on the first call on a device,
+// with that device current).
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GPTQ2D_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return GPTQ2D_ERR_HIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -234,6 +266,30 @@ int gptq2d_quantize(int64_t m, int64_t n, int bits, int dtype, const void* W, co
   return quantize_enqueue(m, n, bits, dtype, W, A, B, scales, codes, Q, ws.ptr, info, s);
 }
 
+int gptq2d_quantize_noalloc(int64_t m, int64_t n, int bits, int dtype, const void* W,
+                            const void* A, const void* B, const void* scales, int8_t* codes,
+                            void* Q, int* info, void* stream) {
+  if (m <= 0 || m > kMaxDim) return -1;
+  if (n <= 0 || n > kMaxDim) return -2;
+  if (bits < 2 || bits > 8) return -3;
+  if (bad_dtype(dtype)) return -4;
+  if (W == nullptr) return -5;
+  if (A == nullptr) return -6;
+  if (B == nullptr) return -7;
+  if (scales == nullptr) return -8;
+  if (codes == nullptr) return -9;
+  if (Q == nullptr) return -10;
+  if (gptq2d_workspace_bytes(m, n, dtype) > kNoAllocBytes) return GPTQ2D_ERR_SCRATCH;
+  void* ws = nullptr;
+  int rc = scratch_address(&ws);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = clear_info(info, s))) return rc;
+  // every counter, flag and accumulator the kernels read before writing is cleared (or
+  // stored before it is read) by the launches themselves, so the previous call's contents
+  // of the buffer do not matter
+  return quantize_enqueue(m, n, bits, dtype, W, A, B, scales, codes, Q, ws, info, s);
+}
 
 size_t gptq2d_workspace3_bytes(int64_t m1, int64_t m2, int64_t m3, int dtype) {
   if (m1 <= 0 || m2 <= 0 || m3 <= 0 || m1 > kMaxDim || m2 > kMaxDim || m3 > kMaxDim ||
@@ -424,6 +480,9 @@ const char* gptq2d_strerror(int st) {
   if (st < 0) return "invalid argument (the negated value is the 1-based argument index)";
   if (st == GPTQ2D_ERR_HIP) return "HIP runtime error while enqueuing work";
   if (st == GPTQ2D_ERR_ALLOC) return "device allocation of the workspace failed";
+  if (st == GPTQ2D_ERR_SCRATCH)
+    return "the problem needs more workspace than the static scratch buffer of "
+           "gptq2d_quantize_noalloc holds (GPTQ2D_NOALLOC_SCRATCH_BYTES)";
   return "unknown status";
 }
 
