@@ -788,14 +788,13 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
     // dependencies (wave 0 waits, the barrier releases the others); every task polls only
     // the few tiles it reads, so the waiters of one step spread over many words
     if (w == 0) {
-      CholWait cw[4];
-      const int nw = chol_waits(n, ct, cw);
       bool ok = true;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (ok && c < nw)
-          ok = chol_wait((cw[c].arr == 0 ? m.tile_cnt : m.xcnt) + cw[c].idx, cw[c].val, a.ctl,
-                         a.info);
+      for (int q = 0; q < 4; ++q) {
+        CholWait cw;
+        if (ok && chol_wait_at(n, ct, q, &cw))
+          ok = chol_wait((cw.arr == 0 ? m.tile_cnt : m.xcnt) + cw.idx, cw.val, a.ctl, a.info);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __syncthreads();

@@ -112,36 +112,52 @@ struct CholWait {
   int64_t idx;
   int val;
 };
-// The conditions task t waits for before it starts (in this order); returns their count
-// (at most 4).  Each names exactly the tiles the task reads:
+// Condition q (0-based) of the conditions task t waits for before it starts, in this order;
+// false when t has fewer than q + 1.  Each names exactly the tiles the task reads:
 //   kind 2: L_i,khi-1 final (so every L_ik, k < khi), X_khi-1,s final (so every X_ks,
 //           s <= k < khi), the tile's previous chunks, and X_ii for the last chunk;
 //   kinds 0, 1: the panel tiles read are final, and the task's own tiles carry the panels
 //           0 .. s - 2.
-G2D_HD inline int chol_waits(int n, const CholTask& t, CholWait* w) {
-  int c = 0;
+// (One condition per call and no array, so that a kernel unrolling q over 0..3 keeps them
+// in registers.)
+G2D_HD inline bool chol_wait_at(int n, const CholTask& t, int q, CholWait* w) {
   const int64_t N = n;
+  int k = 0;  // conditions listed so far
+  bool found = false;
+  auto put = [&](bool present, int arr, int64_t idx, int val) {
+    if (!present) return;
+    if (k == q) {
+      *w = CholWait{arr, idx, val};
+      found = true;
+    }
+    ++k;
+  };
   if (t.kind == 2) {
     int klo, khi;
     xrow_range(t, &klo, &khi);
     const int nch = xrow_chunks(t.i, t.s);
-    w[c++] = CholWait{0, (int64_t)t.i * N + (khi - 1), kFinal};
-    w[c++] = khi - 1 == t.s ? CholWait{0, (int64_t)t.s * N + t.s, kFinal}
-                            : CholWait{1, (int64_t)(khi - 1) * N + t.s, kFinal};
-    if (t.j < nch - 1) w[c++] = CholWait{1, (int64_t)t.i * N + t.s, nch - 1 - t.j};
-    if (t.j == 0) w[c++] = CholWait{0, (int64_t)t.i * N + t.i, kFinal};
-    return c;
+    put(true, 0, (int64_t)t.i * N + (khi - 1), kFinal);
+    if (khi - 1 == t.s)
+      put(true, 0, (int64_t)t.s * N + t.s, kFinal);
+    else
+      put(true, 1, (int64_t)(khi - 1) * N + t.s, kFinal);
+    put(t.j < nch - 1, 1, (int64_t)t.i * N + t.s, nch - 1 - t.j);
+    put(t.j == 0, 0, (int64_t)t.i * N + t.i, kFinal);
+  } else {
+    const int r2 = t.kind == 0 ? t.j : t.s;  // the second panel row read
+    put(t.s >= 1, 0, (int64_t)t.i * N + (t.s - 1), kFinal);
+    put(t.s >= 1 && r2 != t.i, 0, (int64_t)r2 * N + (t.s - 1), kFinal);
+    put(t.kind == 0, 0, (int64_t)t.i * N + t.j, t.s - 1);
+    put(t.kind == 1 && t.s >= 2, 0, (int64_t)t.s * N + t.s, t.s - 1);
+    put(t.kind == 1 && t.s >= 2 && t.i != t.s, 0, (int64_t)t.i * N + t.s, t.s - 1);
   }
-  const int r2 = t.kind == 0 ? t.j : t.s;  // the second panel row read
-  if (t.s >= 1) {
-    w[c++] = CholWait{0, (int64_t)t.i * N + (t.s - 1), kFinal};
-    if (r2 != t.i) w[c++] = CholWait{0, (int64_t)r2 * N + (t.s - 1), kFinal};
-  }
-  if (t.kind == 0) w[c++] = CholWait{0, (int64_t)t.i * N + t.j, t.s - 1};
-  if (t.kind == 1 && t.s >= 2) {
-    w[c++] = CholWait{0, (int64_t)t.s * N + t.s, t.s - 1};
-    if (t.i != t.s) w[c++] = CholWait{0, (int64_t)t.i * N + t.s, t.s - 1};
-  }
+  return found;
+}
+// All conditions of task t (at most 4) into w; returns their count.
+G2D_HD inline int chol_waits(int n, const CholTask& t, CholWait* w) {
+  int c = 0;
+  for (int q = 0; q < 4; ++q)
+    if (chol_wait_at(n, t, q, &w[c])) ++c;
   return c;
 }
 // The counter a finished task sets (a store, never an add): bulk tasks count the panels
