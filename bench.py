@@ -20,7 +20,8 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"hbm_gbs": 8000.0, "fp32_tflops": 157.3, "fp64_tflops": 78.6}
 # Kernel sources whose text the stored HBM-traffic counters belong to.
-TRAFFIC_SOURCES = ("two_sided_adaptive_amd/csrc/sweep.hip", "two_sided_adaptive_amd/csrc/common.hpp")
+TRAFFIC_SOURCES = ("two_sided_adaptive_amd/csrc/sweep.hip", "two_sided_adaptive_amd/csrc/common.hpp",
+                   "two_sided_adaptive_amd/csrc/schedule.hpp")
 METRIC = "quantized weight entries/sec and s/layer, 4096x4096 4-bit GPTQ-2D, 1 MI355X"
 
 
