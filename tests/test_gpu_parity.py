@@ -142,18 +142,25 @@ def test_numerical_failures_reported(g2d):
 
 
 @pytest.mark.parametrize("shape", [(130, 200), (200, 130), (257, 129), (65, 63)])
-def test_workspace_contents_do_not_matter(g2d, shape):
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_workspace_contents_do_not_matter(g2d, shape, dtype):
     # a caller's workspace may hold anything, NaN included: the codes must not depend on it
+    # (fp64: equal to the oracle; fp32: bitwise equal to a run on a zeroed workspace)
     m, n = shape
     bits = 2 + (m * 7 + n) % 7
-    wl = make_random(m, n, bits, seed=m * 1000 + n)
-    W, A, B, s = wl.cast("f64")
-    ref = oracle.quantize(W, A, B, s, bits)
+    wl = make_random(m, n, bits, seed=m * 1000 + n, dtype=dtype)
+    W, A, B, s = wl.cast(dtype)
     tW, tA, tB, ts = _dev(W, A, B, s)
-    need = g2d.workspace_bytes(m, n, torch.float64)
+    tdt = torch.float64 if dtype == "f64" else torch.float32
+    need = g2d.workspace_bytes(m, n, tdt)
+    if dtype == "f64":
+        ref = oracle.quantize(W, A, B, s, bits)["Z"]
+    else:
+        ws0 = torch.zeros((need,), dtype=torch.uint8, device=DEV)
+        ref = g2d.quantize(tW, tA, tB, bits, ts, workspace=ws0)[0].cpu().numpy().astype(np.int32)
     for fill in (float("nan"), float("inf"), 0.0):
-        print(f"case workspace fill {fill} m={m} n={n}", flush=True)
+        print(f"case workspace fill {fill} {dtype} m={m} n={n}", flush=True)
         ws = torch.full((need // 8 + 1,), fill, dtype=torch.float64, device=DEV)
         codes, Q = g2d.quantize(tW, tA, tB, bits, ts, workspace=ws.view(torch.uint8)[:need])
         z = codes.cpu().numpy().astype(np.int32)
-        assert np.array_equal(z, ref["Z"]), f"fill {fill}: {int(np.sum(z != ref['Z']))} mismatches"
+        assert np.array_equal(z, ref), f"fill {fill}: {int(np.sum(z != ref))} mismatches"
