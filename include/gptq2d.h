@@ -145,9 +145,13 @@ int gptq2d_quantize_noalloc(int64_t m, int64_t n, int bits, int dtype, const voi
  * page, Abstract: the algorithm extends to Hessians with any number of Kronecker
  * factors).  W is an m1 x m2 x m3 tensor (row-major: the last index is fastest) and the
  * Gram of its vectorisation is A1 (x) A2 (x) A3; the result is the trajectory of
- * one-dimensional GPTQ on that vectorisation, in that order.  Rounded slab by slab:
- * slab k (the m2 x m3 matrix W[k]) receives the feedback of the earlier slabs through
- * U1', then is rounded as a two-factor problem under (A2, A3) by the sweep.
+ * one-dimensional GPTQ on that vectorisation, in that order.  When U1' (x) U2' takes at
+ * most 4 GiB (m1 m2 <= 23170 in F64, <= 32768 in F32) the tensor is rounded as one
+ * (m1 m2) x m3 two-factor problem under (A1 (x) A2, A3), whose unit factor is
+ * U1' (x) U2'; above that, slab by slab: slab k (the m2 x m3 matrix W[k]) receives the
+ * feedback of the earlier slabs through U1', then is rounded as a two-factor problem
+ * under (A2, A3).  Both routes give the same trajectory; gptq2d_workspace3_bytes sizes
+ * the route the call takes.
  *   m1, m2, m3  tensor extents, each in [1, 262140]                   [args 1-3]
  *   bits, dtype                                                        [args 4-5]
  *   W        m1 x m2 x m3                                               [arg 6]
@@ -156,7 +160,8 @@ int gptq2d_quantize_noalloc(int64_t m, int64_t n, int bits, int dtype, const voi
  *   codes    m1 x m2 x m3 int8 out; Q m1 x m2 x m3 out (dtype)       [args 11-12]
  *   workspace, workspace_bytes (gptq2d_workspace3_bytes), info, stream [args 13-16]
  * info[0] = 5, 6 or 7 if A1, A2 or A3 is not positive definite; 3 for a bad scale, with
- * info[1] the 1-based index of the row within its slab; 4 as above.
+ * info[1] the 1-based index k m2 + i + 1 of a fibre W[k][i][:] whose scale is bad; 4 as
+ * above.
  */
 int gptq2d_quantize3(int64_t m1, int64_t m2, int64_t m3, int bits, int dtype, const void* W,
                      const void* A1, const void* A2, const void* A3, const void* scales,

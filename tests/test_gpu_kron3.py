@@ -42,9 +42,12 @@ def test_k1_fp64_exact(g2d):
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 1), (1, 65, 63), (5, 1, 70), (20, 70, 1),
-                                   (17, 33, 40), (37, 20, 24), (3, 130, 66)])
+                                   (17, 33, 40), (37, 20, 24), (3, 130, 66),
+                                   (37, 640, 24), (32, 1024, 40)])
 def test_ragged_shapes_fp64_exact(g2d, shape):
-    # m1 = 17 and 37 leave ragged blocks of the lazy slab feedback (16 slabs a block)
+    # Up to m1 m2 = 23170 rows (fp64) the call sweeps the stacked (m1 m2) x m3 matrix under
+    # U1' (x) U2'; the last two shapes are above that and take the slab-by-slab route, where
+    # m1 = 37 leaves a ragged block of the lazy slab feedback (16 slabs a block).
     bits = 2 + sum(shape) % 7
     wl = make_random3(*shape, bits, seed=shape[0] * 10007 + shape[1] * 101 + shape[2])
     xs, z, Q = _run(g2d, wl)
@@ -85,3 +88,38 @@ def test_k2_full_size_fp64_exact(g2d):
     ref = oracle.quantize3(*xs, wl.bits)
     assert np.array_equal(z, ref["Z"]), f"{int(np.sum(z != ref['Z']))} mismatches"
     np.testing.assert_array_equal(Q, ref["Q"])
+
+
+@pytest.mark.parametrize("shape", [(6, 130, 40), (37, 640, 24)])
+def test_workspace_contents_do_not_matter(g2d, shape):
+    # a caller's workspace may hold anything, NaN included (the stacked route leaves the
+    # tiles of U1' (x) U2' below its diagonal unwritten; the slab route keeps its slab
+    # buffer there): the codes must still equal the oracle's
+    bits = 4
+    wl = make_random3(*shape, bits, seed=sum(shape))
+    xs = [np.ascontiguousarray(x, dtype=np.float64) for x in (wl.W, wl.A1, wl.A2, wl.A3,
+                                                                wl.scales)]
+    t = [torch.from_numpy(x).to(DEV) for x in xs]
+    ref = oracle.quantize3(*xs, bits)["Z"]
+    need = g2d.load_library().gptq2d_workspace3_bytes(*shape, 1)
+    for fill in (float("nan"), float("inf")):
+        print(f"case workspace fill {fill} shape={shape}", flush=True)
+        ws = torch.full((need // 8 + 1,), fill, dtype=torch.float64, device=DEV)
+        codes, _ = g2d.quantize3(t[0], t[1], t[2], t[3], bits, t[4],
+                                 workspace=ws.view(torch.uint8)[:need])
+        z = codes.cpu().numpy().astype(np.int32)
+        assert np.array_equal(z, ref), f"fill {fill}: {int(np.sum(z != ref))} mismatches"
+
+
+@pytest.mark.parametrize("shape", [(6, 130, 40), (37, 640, 24)])
+def test_bad_scale_reported_by_fibre(g2d, shape):
+    # both routes name the fibre W[k][i][:] by k m2 + i + 1
+    wl = make_random3(*shape, 4, seed=5)
+    sc = wl.scales.copy()
+    sc[2, 5] = 0.0
+    t = [torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+         for x in (wl.W, wl.A1, wl.A2, wl.A3, sc)]
+    print(f"case bad scale shape={shape}", flush=True)
+    with pytest.raises(g2d.GPTQ2DError, match=f"scale of row {2 * shape[1] + 6} "):
+        g2d.quantize3(t[0], t[1], t[2], t[3], 4, t[4])
+    torch.cuda.synchronize()
