@@ -88,6 +88,7 @@ struct SweepArgs {
   int nxcd;   // XCDs of the device (<= kMaxXcd)
   int nbxcd;  // band workers per XCD
   int gs;     // bands are dealt to the XCDs in groups of gs consecutive bands
+  int near_mod;  // of the workgroups past the band workers, one in near_mod takes near tasks
   const T* Ua;
   const T* Ub;
   const T* s;
@@ -1129,7 +1130,7 @@ __global__ __launch_bounds__(kThreads) void k_sweep(SweepArgs<T> a) {
   const int r = tk - 3 - a.nbxcd;
   const int cls = tk < 3 ? (tk == 0 ? kFar : tk == 1 ? kNear : kNext)
                   : r < 0 ? kFar
-                  : r % 7 == 0 ? kNear
+                  : r % a.near_mod == 0 ? kNear
                   : r % 20 == 5 ? kNext : kFar;
   gemm_worker<T>(a, *reinterpret_cast<GemmSmem<T>*>(smem), cls);
 }
@@ -1202,8 +1203,13 @@ SyncLayout sync_layout(int64_t m, int64_t n) {
 // default (b0, gs0) keeps every band of the pipeline active at once and is kept unless
 // another plan is estimated at least 10 % faster.  GPTQ2D_SWEEP_BANDS="b,gs" overrides the
 // plan (a tuning knob; values are clamped to what the grid allows).
+// Of the update workgroups, one in seven takes near tasks when the pipeline bounds the
+// sweep (their latency is then on the critical path: fewer near workers made the
+// 4096-wide layer slower); when the updates bound it, one in fourteen, which leaves more
+// CUs to the far tasks (the 8192-wide and 14336 x 4096 layers were 4-6 % faster).
+// GPTQ2D_SWEEP_NEAR=k overrides (k >= 1).
 struct BandPlan {
-  int b, gs;
+  int b, gs, near_mod;
 };
 double pipeline_phases(int Mb, int Nj, int nx, int b, int gs) {
   std::vector<double> free_at((size_t)nx * b, 0.0);
@@ -1224,12 +1230,17 @@ double pipeline_phases(int Mb, int Nj, int nx, int b, int gs) {
 BandPlan plan_bands(int64_t m, int64_t n, int Mb, int Nj, int nx, int grid, int b0, int gs0,
                     bool f64) {
   const int bmax = grid / nx - NCLS;
-  BandPlan best{b0, gs0};
+  BandPlan best{b0, gs0, 7};
+  int near_env = 0;
+  if (const char* env = getenv("GPTQ2D_SWEEP_NEAR")) {
+    if (sscanf(env, "%d", &near_env) != 1 || near_env < 1) near_env = 0;
+  }
   if (const char* env = getenv("GPTQ2D_SWEEP_BANDS")) {
     int b = 0, gs = 0;
     if (sscanf(env, "%d,%d", &b, &gs) == 2 && b >= 1 && gs >= 1) {
       best.b = b < bmax ? b : bmax;
       best.gs = gs;
+      if (near_env) best.near_mod = near_env;
       return best;
     }
   }
@@ -1241,6 +1252,9 @@ BandPlan plan_bands(int64_t m, int64_t n, int Mb, int Nj, int nx, int grid, int 
     const double tg = flops / (rate * (double)(grid - nx * b));
     return tp > tg ? tp : tg;
   };
+  auto update_bound = [&](int b, int gs) {
+    return flops / (rate * (double)(grid - nx * b)) > pipeline_phases(Mb, Nj, nx, b, gs) * phase;
+  };
   const double t0 = est(b0, gs0);
   double tb = t0;
   for (int gs = gs0; gs >= 1; gs /= 2)
@@ -1248,10 +1262,11 @@ BandPlan plan_bands(int64_t m, int64_t n, int Mb, int Nj, int nx, int grid, int 
       const double t = est(b, gs);
       if (t < tb) {
         tb = t;
-        best = BandPlan{b, gs};
+        best = BandPlan{b, gs, 7};
       }
     }
-  if (tb > 0.9 * t0) best = BandPlan{b0, gs0};
+  if (tb > 0.9 * t0) best = BandPlan{b0, gs0, 7};
+  best.near_mod = near_env ? near_env : update_bound(best.b, best.gs) ? 14 : 7;
   return best;
 }
 
@@ -1337,6 +1352,7 @@ hipError_t sweep_typed(int64_t m, int64_t n, int bits, const T* W, const T* Ua, 
   const BandPlan bp = plan_bands(m, n, a.Mb, a.Nj, nx, grid, b0, gs0, sizeof(T) == 8);
   a.gs = bp.gs;
   a.nbxcd = bp.b;
+  a.near_mod = bp.near_mod;
   if (a.nbxcd < 1) return hipErrorInvalidConfiguration;
 
   const bool pr = prof_on();
