@@ -75,6 +75,20 @@ static int check_factor(const std::vector<int>& ns) {
             return fail(msg);
           }
         }
+        // the trailing updates of a tile take the panels 0 .. s - 2 exactly once, in order:
+        // a bulk task finds its tile carrying exactly the panels before its first one, and a
+        // panel step finds its own tile carrying exactly the panels 0 .. s - 2
+        {
+          const int own = t.kind == 0 ? cnt[q][0][(size_t)t.i * n + t.j]
+                                      : t.kind == 1 ? cnt[q][0][(size_t)t.i * n + t.s] : 0;
+          const int want = t.kind == 0 ? bulk_lo(t.j, t.s) : t.kind == 1 ? (t.s >= 1 ? t.s - 1 : 0) : 0;
+          if (t.kind != 2 && own != want) {
+            snprintf(msg, sizeof msg,
+                     "factor n=%d step %d: task kind %d (i=%d s=%d j=%d) finds its tile after "
+                     "%d panels, expected %d", n, g, t.kind, t.i, t.s, t.j, own, want);
+            return fail(msg);
+          }
+        }
         const CholWait sg = chol_signal(n, t);
         int& v = cnt[q][sg.arr][sg.idx];
         if (sg.val < v) {

@@ -267,14 +267,21 @@ __device__ inline void st_u(void* U, bool f32, int64_t idx, double v) {
     ((double*)U)[idx] = v;
 }
 
-// The trailing update of one tile by one panel: A_ij -= L_ik L_jk^T (64 x 64 tiles of the
-// reversed matrix, k = panel block column).
-__device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar, const double* Lt,
-                                 const void* A, bool f32, TileSmem<double>& sm) {
+// LDS of a trailing-update task: two stages of a 32-deep chunk of both operands, k-major.
+struct BulkSmem {
+  double a[2][kKc][kTile + kPad];
+  double b[2][kKc][kTile + kPad];
+};
+
+// The trailing update of one tile by the panels k0 .. k1 - 1: A_ij -= sum_k L_ik L_jk^T
+// (64 x 64 tiles of the reversed matrix, k = panel block column).  The tile is read once
+// (from A itself when k0 = 0: no update has touched it) and written once; the panel tiles
+// stream through LDS in 32-deep chunks, the next chunk's loads in flight while the current
+// one is multiplied.
+__device__ inline void chol_bulk(int64_t p, int k0, int k1, int i, int j, double* Ar,
+                                 const double* Lt, const void* A, bool f32, BulkSmem& sm) {
   const int64_t ri = (int64_t)i * NB, cj = (int64_t)j * NB;
   const int M = tile_rows(p, i), N = tile_rows(p, j);
-  // both operands i-major 64 x 64 from Lt, staged k-major through LDS in two chunks; the
-  // tile itself at device scope
   typedef Mfma<double>::acc_t acc_t;
   // an opaque copy of the thread index: values derived from it are recomputed per task
   // instead of being held (and spilled) across the persistent loop
@@ -282,23 +289,35 @@ __device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar, con
   __asm__ volatile("" : "+v"(tid));
   const int lane = tid & 63, w = tid >> 6;
   const int wr = w >> 1, wc = w & 1, kr = lane >> 4, cl = lane & 15;
-  const rsrc_t ra = make_rsrc(lt_tile(Lt, i, k), (int64_t)M * NB * 8);
-  const rsrc_t rb = make_rsrc(lt_tile(Lt, j, k), (int64_t)N * NB * 8);
   const rsrc_t rc = make_rsrc(Ar + ri * p + cj, ((int64_t)(M - 1) * p + N) * 8);
+  const int i4 = tid >> 2, k8 = (tid & 3) * 8;
+  // chunk c: half c & 1 of panel k0 + c / 2, both operands i-major 64 x 64 in Lt
+  double va[8], vb[8];
+  auto fetch = [&](int c) {
+    const int k = k0 + (c >> 1), h = c & 1;
+    const rsrc_t ra = make_rsrc(lt_tile(Lt, i, k), (int64_t)M * NB * 8);
+    const rsrc_t rb = make_rsrc(lt_tile(Lt, j, k), (int64_t)N * NB * 8);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      va[u] = ld<false>(ra, (uint32_t)(i4 * NB + 32 * h + k8 + u));
+      vb[u] = ld<false>(rb, (uint32_t)(i4 * NB + 32 * h + k8 + u));
+    }
+  };
+  auto stage = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sm.a[st][k8 + u][i4] = va[u];
+      sm.b[st][k8 + u][i4] = vb[u];
+    }
+  };
   acc_t acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = acc_t{0, 0, 0, 0};
-  const int i4 = tid >> 2, k8 = (tid & 3) * 8;
-  double va[2][8], vb[2][8], old[2][2][4];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      va[h][u] = ld<false>(ra, (uint32_t)(i4 * NB + 32 * h + k8 + u));
-      vb[h][u] = ld<false>(rb, (uint32_t)(i4 * NB + 32 * h + k8 + u));
-    }
+  const int nc = 2 * (k1 - k0);
+  fetch(0);
+  double old[2][2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -306,25 +325,25 @@ __device__ inline void chol_bulk(int64_t p, int k, int i, int j, double* Ar, con
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = 32 * wr + 16 * a + Mfma<double>::row(lane, e), jj = 32 * wc + 16 * b + cl;
-        // (panel 0 is the tile's first update: the tile is read from A itself)
-        old[a][b][e] = k == 0 ? ld_src(A, f32, p, ri + ii, cj + jj)
-                              : ld<true>(rc, (uint32_t)((int64_t)ii * p + jj));
+        old[a][b][e] = k0 == 0 ? ld_src(A, f32, p, ri + ii, cj + jj)
+                               : ld<true>(rc, (uint32_t)((int64_t)ii * p + jj));
       }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      sm.a[k8 + u][i4] = va[h][u];
-      sm.b[k8 + u][i4] = vb[h][u];
+  stage(0);
+  if (nc > 1) fetch(1);
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    const int st = c & 1;
+    if (c + 1 < nc) {
+      stage(st ^ 1);  // (stage st ^ 1 was last read before the previous barrier)
+      if (c + 2 < nc) fetch(c + 2);
     }
-    __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kKc; kk += 4) {
       double av[2], bv[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        av[t] = sm.a[kk + kr][32 * wr + 16 * t + cl];
-        bv[t] = sm.b[kk + kr][32 * wc + 16 * t + cl];
+        av[t] = sm.a[st][kk + kr][32 * wr + 16 * t + cl];
+        bv[t] = sm.b[st][kk + kr][32 * wc + 16 * t + cl];
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -708,7 +727,7 @@ __device__ inline int ld_uniform(const int* p) { return __builtin_amdgcn_readfir
 __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
   __shared__ union {
     BlockSmem b;
-    TileSmem<double> t;
+    BulkSmem t;
   } sh;
   __shared__ int task[4];  // kind, matrix, row tile, step (or column) << 16 | column (or jj)
   const int tid = threadIdx.x, lane = tid & 63;
@@ -807,7 +826,7 @@ __global__ __launch_bounds__(256, 2) void k_chol_persistent(CholArgs a) {
     else if (kind == 0 && j == s + 1)
       __builtin_amdgcn_s_setprio(2);
     if (kind == 0)
-      chol_bulk(p, s - 1, i, j, m.Ar, m.Lt, m.A, f32, sh.t);
+      chol_bulk(p, bulk_lo(j, s), s, i, j, m.Ar, m.Lt, m.A, f32, sh.t);
     else if (kind == 1)
       chol_crit(p, s, i, m.Ar, m.Lt, m.Xt, m.A, m.U, f32, a.info, m.side_code, sh.b);
     else

@@ -21,9 +21,10 @@ namespace sched {
 // ---------------------------------------------------------------------------
 // Tiles are 64 x 64; n = tiles per edge.  Tasks of one matrix, step g (groups go by step,
 // the matrices alternating; inside a group the tasks below are listed in this order):
-//   bulk (kind 0): tile (i, j), g + 1 <= j <= i, takes panel g - 1: first the tiles of
-//                  column g + 1 (the look-ahead), after the panel steps the others column by
-//                  column;
+//   bulk (kind 0): tile (i, j), g + 1 <= j <= i, takes the panels bulk_lo(j, g) .. g - 1
+//                  in one task, in the steps bulk_at names: first the tiles of column g + 1
+//                  (the look-ahead, one panel), after the panel steps those of the later
+//                  columns that take a task in step g, column by column;
 //   crit (kind 1): the panel step of row tile i >= g of block column g;
 //   xrow (kind 2): chunk jj of tile (i, s) of X = L^-1, i = g + kInvStride jj, in order of
 //                  jj and s.  Chunk 0, the last one added, covers k in [i - kInvFirst, i) and
@@ -33,12 +34,35 @@ constexpr int kInvDepth = 8;   // tiles of k per chunk of the row inverse
 constexpr int kInvFirst = 8;   // tiles of k of a row's last chunk
 constexpr int kInvStride = 2;  // steps between the chunks of one row (<= kInvFirst + 1)
 constexpr int kFinal = 1 << 24;  // tile counter of a final tile
+// The trailing update of a tile column is deferred and applied kBulkDepth panels at a time
+// (one task reads the tile once and multiplies kBulkDepth panel pairs), except in the two
+// steps before the column's own panel step: there the column takes what is left (the
+// flush) and then the last panel alone (the look-ahead, which feeds the panel chain).
+constexpr int kBulkDepth = 16;
 
-// Tasks of the Cholesky in group g: n - g - 1 + n - g + (n - g - 2)(n - g - 1) / 2
-// = u (u + 1) / 2 with u = n - g for g >= 1, and n for g = 0 (panel steps only).
+// Whether tile column j takes a trailing-update task in step g: the steps g = kBulkDepth q
+// up to j - 3, then j - 2 and j - 1 (the panels 0 .. j - 2 in all; the panel step of
+// column j applies panel j - 1 itself).
+G2D_HD inline bool bulk_at(int j, int g) {
+  if (g < 1 || g > j - 1) return false;
+  return g >= j - 2 || g % kBulkDepth == 0;
+}
+// First panel of column j's task in step g (bulk_at(j, g)): the task takes the panels
+// bulk_lo .. g - 1, the ones after its previous task's (0 for the column's first task).
+G2D_HD inline int bulk_lo(int j, int g) {
+  if (g == j - 1) return j - 2 >= 1 ? j - 2 : 0;
+  return ((g - 1) / kBulkDepth) * kBulkDepth;
+}
+
+// Tasks of the Cholesky in group g >= 1 with u = n - g: u - 1 look-ahead tiles, u panel
+// steps, and the tiles of the later columns that take a task: all of them,
+// (u - 2)(u - 1) / 2, when g is a multiple of kBulkDepth, else column g + 2 alone (its
+// flush), u - 2.  Group 0: the n panel steps only.
 G2D_HD inline int64_t chol_group_size(int n, int g) {
   const int64_t u = n - g;
-  return g == 0 ? n : u * (u + 1) / 2;
+  if (g == 0) return n;
+  const int64_t rest = g % kBulkDepth == 0 ? (u - 2) * (u - 1) / 2 : (u >= 2 ? u - 2 : 0);
+  return (u - 1) + u + rest;
 }
 // xrow tasks of chunk jj in group g (row i = g + kInvStride jj): chunk 0 of every s < g;
 // for jj >= 1 the columns s < khi = g - (kInvDepth - kInvStride) jj + kInvDepth - kInvFirst
@@ -59,8 +83,8 @@ G2D_HD inline int xrow_chunks(int i, int s) {
   return 1 + (i - s > kInvFirst ? (i - s - kInvFirst + kInvDepth - 1) / kInvDepth : 0);
 }
 
-// One task: kind 0 bulk of tile (i, j) by panel s - 1; kind 1 the panel step of row tile i
-// of block column s; kind 2 chunk j of tile (i, s) of X.
+// One task: kind 0 bulk of tile (i, j) by the panels bulk_lo(j, s) .. s - 1; kind 1 the
+// panel step of row tile i of block column s; kind 2 chunk j of tile (i, s) of X.
 struct CholTask {
   int kind, i, s, j;
 };
@@ -77,9 +101,11 @@ G2D_HD inline CholTask chol_decode(int n, int g, int64_t r) {
   } else if (k < cg) {
     k -= c1 + c2;
     int j = g + 2;
-    while (k >= n - j && j < n) {
-      k -= n - j;
-      ++j;
+    if (g % kBulkDepth == 0) {
+      while (k >= n - j && j < n) {
+        k -= n - j;
+        ++j;
+      }
     }
     t = CholTask{0, j + k, g, j};
   } else {
@@ -116,8 +142,9 @@ struct CholWait {
 // false when t has fewer than q + 1.  Each names exactly the tiles the task reads:
 //   kind 2: L_i,khi-1 final (so every L_ik, k < khi), X_khi-1,s final (so every X_ks,
 //           s <= k < khi), the tile's previous chunks, and X_ii for the last chunk;
-//   kinds 0, 1: the panel tiles read are final, and the task's own tiles carry the panels
-//           0 .. s - 2.
+//   kinds 0, 1: the panel tiles read are final (for kind 0 the last one, panel s - 1: a
+//           row's panel tiles become final in order), and the task's own tiles carry the
+//           panels before its first one (kind 0: bulk_lo(j, s); kind 1: s - 1).
 // (One condition per call and no array, so that a kernel unrolling q over 0..3 keeps them
 // in registers.)
 G2D_HD inline bool chol_wait_at(int n, const CholTask& t, int q, CholWait* w) {
@@ -147,7 +174,7 @@ G2D_HD inline bool chol_wait_at(int n, const CholTask& t, int q, CholWait* w) {
     const int r2 = t.kind == 0 ? t.j : t.s;  // the second panel row read
     put(t.s >= 1, 0, (int64_t)t.i * N + (t.s - 1), kFinal);
     put(t.s >= 1 && r2 != t.i, 0, (int64_t)r2 * N + (t.s - 1), kFinal);
-    put(t.kind == 0, 0, (int64_t)t.i * N + t.j, t.s - 1);
+    put(t.kind == 0 && bulk_lo(t.j, t.s) > 0, 0, (int64_t)t.i * N + t.j, bulk_lo(t.j, t.s));
     put(t.kind == 1 && t.s >= 2, 0, (int64_t)t.s * N + t.s, t.s - 1);
     put(t.kind == 1 && t.s >= 2 && t.i != t.s, 0, (int64_t)t.i * N + t.s, t.s - 1);
   }
