@@ -19,50 +19,61 @@ namespace sched {
 // ---------------------------------------------------------------------------
 // Factor stage: the persistent Cholesky + row inverse (k_chol_persistent)
 // ---------------------------------------------------------------------------
-// Tiles are 64 x 64; n = tiles per edge.  Tasks of one matrix, step g (groups go by step,
-// the matrices alternating; inside a group the tasks below are listed in this order):
-//   bulk (kind 0): tile (i, j), g + 1 <= j <= i, takes the panels bulk_lo(j, g) .. g - 1
-//                  in one task, in the steps bulk_at names: first the tiles of column g + 1
-//                  (the look-ahead, one panel), after the panel steps those of the later
-//                  columns that take a task in step g, column by column;
-//   crit (kind 1): the panel step of row tile i >= g of block column g;
+// Tiles are 64 x 64; n = tiles per edge.  The tasks of one matrix (groups go by step, the
+// matrices alternating; chol_segments gives the order inside a group):
+//   bulk (kind 0): tile (i, j) in step s, s + 1 <= j <= i, takes the panels
+//                  bulk_lo(j, s) .. s - 1 in one task, in the steps bulk_at names;
+//   crit (kind 1): the panel step of row tile i of block column s;
 //   xrow (kind 2): chunk jj of tile (i, s) of X = L^-1, i = g + kInvStride jj, in order of
 //                  jj and s.  Chunk 0, the last one added, covers k in [i - kInvFirst, i) and
 //                  multiplies by -X_ii; chunk jj >= 1 covers kInvDepth tiles below
 //                  khi = i - kInvFirst - kInvDepth (jj - 1), all clipped at s.
-constexpr int kInvDepth = 8;   // tiles of k per chunk of the row inverse
+constexpr int kInvDepth = 16;  // tiles of k per chunk of the row inverse
 constexpr int kInvFirst = 8;   // tiles of k of a row's last chunk
 constexpr int kInvStride = 2;  // steps between the chunks of one row (<= kInvFirst + 1)
 constexpr int kFinal = 1 << 24;  // tile counter of a final tile
 // The trailing update of a tile column is deferred and applied kBulkDepth panels at a time
-// (one task reads the tile once and multiplies kBulkDepth panel pairs), except in the two
-// steps before the column's own panel step: there the column takes what is left (the
-// flush) and then the last panel alone (the look-ahead, which feeds the panel chain).
+// (one task reads the tile once and multiplies kBulkDepth panel pairs), except in the
+// kBulkNear - 1 steps before the column's own panel step, where it takes one panel per
+// step (the last of them is the look-ahead, which feeds the panel chain).  The deep tasks
+// of column j sit in the steps j - kBulkNear - q kBulkDepth (q >= 0), so that the last
+// one ends kBulkNear - 1 steps before the panel step needs the tile, and the deep tasks of
+// different columns fall in different steps: every step carries about the same work.
 constexpr int kBulkDepth = 16;
+constexpr int kBulkNear = 3;
 
-// Whether tile column j takes a trailing-update task in step g: the steps g = kBulkDepth q
-// up to j - 3, then j - 2 and j - 1 (the panels 0 .. j - 2 in all; the panel step of
-// column j applies panel j - 1 itself).
+// Whether tile column j takes a trailing-update task in step g (the panels 0 .. j - 2 in
+// all; the panel step of column j applies panel j - 1 itself).
 G2D_HD inline bool bulk_at(int j, int g) {
   if (g < 1 || g > j - 1) return false;
-  return g >= j - 2 || g % kBulkDepth == 0;
+  return g > j - kBulkNear || (j - kBulkNear - g) % kBulkDepth == 0;
 }
 // First panel of column j's task in step g (bulk_at(j, g)): the task takes the panels
 // bulk_lo .. g - 1, the ones after its previous task's (0 for the column's first task).
 G2D_HD inline int bulk_lo(int j, int g) {
-  if (g == j - 1) return j - 2 >= 1 ? j - 2 : 0;
-  return ((g - 1) / kBulkDepth) * kBulkDepth;
+  const int prev = g > j - kBulkNear ? g - 1 : g - kBulkDepth;
+  return prev >= 1 ? prev : 0;
+}
+// Group g lists, in this order: the look-ahead of step g (column g + 1, one panel), the
+// panel steps of column g, the one-panel tasks of columns g + 2 .. g + kBulkNear - 1, the
+// deep tasks of columns g + kBulkNear + q kBulkDepth, then the inverse chunks.  Sizes of the
+// first four segments:
+G2D_HD inline void chol_segments(int n, int g, int64_t* seg) {
+  auto tiles = [&](int j) { return (int64_t)(j <= n - 1 ? n - j : 0); };  // tiles of column j
+  seg[0] = g >= 1 ? tiles(g + 1) : 0;
+  seg[1] = n - g;
+  seg[2] = 0;
+  seg[3] = 0;
+  if (g == 0) return;
+  for (int j = g + 2; j < g + kBulkNear; ++j) seg[2] += tiles(j);
+  for (int j = g + kBulkNear; j <= n - 1; j += kBulkDepth) seg[3] += tiles(j);
 }
 
-// Tasks of the Cholesky in group g >= 1 with u = n - g: u - 1 look-ahead tiles, u panel
-// steps, and the tiles of the later columns that take a task: all of them,
-// (u - 2)(u - 1) / 2, when g is a multiple of kBulkDepth, else column g + 2 alone (its
-// flush), u - 2.  Group 0: the n panel steps only.
+// Tasks of the Cholesky in group g (the four segments).
 G2D_HD inline int64_t chol_group_size(int n, int g) {
-  const int64_t u = n - g;
-  if (g == 0) return n;
-  const int64_t rest = g % kBulkDepth == 0 ? (u - 2) * (u - 1) / 2 : (u >= 2 ? u - 2 : 0);
-  return (u - 1) + u + rest;
+  int64_t seg[4];
+  chol_segments(n, g, seg);
+  return seg[0] + seg[1] + seg[2] + seg[3];
 }
 // xrow tasks of chunk jj in group g (row i = g + kInvStride jj): chunk 0 of every s < g;
 // for jj >= 1 the columns s < khi = g - (kInvDepth - kInvStride) jj + kInvDepth - kInvFirst
@@ -92,24 +103,29 @@ struct CholTask {
 G2D_HD inline CholTask chol_decode(int n, int g, int64_t r) {
   CholTask t{-1, 0, 0, 0};
   int k = (int)r;
-  const int c1 = g >= 1 ? n - g - 1 : 0, c2 = n - g;
-  const int64_t cg = chol_group_size(n, g);
-  if (k < c1) {
+  int64_t seg[4];
+  chol_segments(n, g, seg);
+  const int64_t cg = seg[0] + seg[1] + seg[2] + seg[3];
+  if (k < seg[0]) {
     t = CholTask{0, g + 1 + k, g, g + 1};
-  } else if (k < c1 + c2) {
-    t = CholTask{1, g + (k - c1), g, 0};
-  } else if (k < cg) {
-    k -= c1 + c2;
+  } else if ((k -= (int)seg[0]) < seg[1]) {
+    t = CholTask{1, g + k, g, 0};
+  } else if ((k -= (int)seg[1]) < seg[2]) {
     int j = g + 2;
-    if (g % kBulkDepth == 0) {
-      while (k >= n - j && j < n) {
-        k -= n - j;
-        ++j;
-      }
+    while (k >= n - j) {
+      k -= n - j;
+      ++j;
+    }
+    t = CholTask{0, j + k, g, j};
+  } else if ((k -= (int)seg[2]) < seg[3]) {
+    int j = g + kBulkNear;
+    while (k >= n - j) {
+      k -= n - j;
+      j += kBulkDepth;
     }
     t = CholTask{0, j + k, g, j};
   } else {
-    k -= (int)cg;
+    k = (int)(r - cg);
     int jj = 0;
     if (k >= xrow_count(n, g, 0)) {
       k -= xrow_count(n, g, 0);
