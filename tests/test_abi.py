@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
 
 
 def test_every_declared_symbol_is_exported(lib):
-    raw = ctypes.CDLL(os.path.join(ROOT, "two_sided_adaptive_amd", "libgptq2d.so"))
+    import two_sided_adaptive_amd as g2d
+    raw = ctypes.CDLL(g2d.LIB_PATH)
     for name in declared_functions():
         assert hasattr(raw, name), name
 

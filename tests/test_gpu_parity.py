@@ -121,6 +121,29 @@ def test_repeat_is_bitwise_deterministic(g2d):
         assert np.array_equal(z1, z2) and np.array_equal(q1, q2)
 
 
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_scheduling_knobs_do_not_change_results(g2d, dtype, monkeypatch):
+    # The sweep's run-time plan (band workers per XCD and consecutive bands per XCD, the
+    # share of update workgroups taking near tasks) decides which workgroup does what and
+    # when, never the order of any sum: codes and Q are bitwise those of the default plan.
+    wl = make_random(700, 650, 4, seed=21)
+    _, z0, q0 = _run(g2d, wl, dtype)
+    if dtype == "f64":
+        W, A, B, s = wl.cast(dtype)
+        assert np.array_equal(z0, oracle.quantize(W, A, B, s, 4)["Z"])
+    for bands, near in (("1,1", None), ("2,4", None), ("3,2", "1"), (None, "3"),
+                        (None, "1000"), ("6,1", "14")):
+        for var, val in (("GPTQ2D_SWEEP_BANDS", bands), ("GPTQ2D_SWEEP_NEAR", near)):
+            if val is None:
+                monkeypatch.delenv(var, raising=False)
+            else:
+                monkeypatch.setenv(var, val)
+        print(f"case plan bands={bands} near={near} {dtype}", flush=True)
+        _, z, q = _run(g2d, wl, dtype)
+        assert np.array_equal(z, z0), f"bands={bands} near={near}: codes differ"
+        assert np.array_equal(q.view(np.uint8), q0.view(np.uint8)), f"bands={bands} near={near}: Q"
+
+
 def test_numerical_failures_reported(g2d):
     wl = make_random(40, 30, 4, seed=4)
     W, A, B, s = wl.cast("f64")

@@ -13,7 +13,9 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgptq2d.so")
+# the in-tree build; GPTQ2D_LIB names another build of the same library (a debug or
+# sanitizer build, say)
+LIB_PATH = os.environ.get("GPTQ2D_LIB") or os.path.join(_PKG, "libgptq2d.so")
 F32, F64 = 0, 1
 _lib = None
 
