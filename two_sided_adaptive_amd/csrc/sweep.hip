@@ -550,23 +550,42 @@ __device__ inline void round_micro_tile(const SweepArgs<T>& a, BandSmem<T>& sm, 
 
   // feedback from outside the micro-tile (MFMA), two chains per product
   {
+    // The LDS operands of each pair of products are read one pair ahead, before the
+    // (wave-uniform) test that skips the pair, so that a read's latency passes while the
+    // products before it run.  (Reads past the pairs a wave uses return data it ignores.)
     acc_t v0 = acc_t{0, 0, 0, 0}, v1 = acc_t{0, 0, 0, 0};
     // earlier micro-rows of this band, same micro-column (written in earlier phases)
+    {
+      T r0 = sm.rT[s4][cl][kq], r1 = sm.rT[s4][cl][4 + kq];
 #pragma unroll
-    for (int s = 0; s < 3 * MU / 4; s += 2) {
-      if (s < 4 * w) {
-        v0 = Mfma<T>::run(aVi[s], sm.rT[s4][cl][4 * s + kq], v0);
-        v1 = Mfma<T>::run(aVi[s + 1], sm.rT[s4][cl][4 * s + 4 + kq], v1);
+      for (int s = 0; s < 3 * MU / 4; s += 2) {
+        const T c0 = r0, c1 = r1;
+        if (s + 2 < 3 * MU / 4) {
+          r0 = sm.rT[s4][cl][4 * s + 8 + kq];
+          r1 = sm.rT[s4][cl][4 * s + 12 + kq];
+        }
+        if (s < 4 * w) {
+          v0 = Mfma<T>::run(aVi[s], c0, v0);
+          v1 = Mfma<T>::run(aVi[s + 1], c1, v1);
+        }
       }
     }
     acc_t h0 = acc_t{0, 0, 0, 0}, h1 = acc_t{0, 0, 0, 0};
     // the band's Delta over the window columns (this wave's rows) times U'b
+    {
+      auto dop = [&](int k) { return sm.dh[w][(clo + (k >> 4)) & 7][cl][k & 15]; };
+      T d0 = dop(kq), d1 = dop(4 + kq);
 #pragma unroll
-    for (int s = 0; s < 7 * MU / 4; s += 2) {
-      if (s < 4 * nwin) {
-        const int k0 = 4 * s + kq, k1 = 4 * s + 4 + kq;
-        h0 = Mfma<T>::run(sm.dh[w][(clo + (k0 >> 4)) & 7][cl][k0 & 15], bwin[s], h0);
-        h1 = Mfma<T>::run(sm.dh[w][(clo + (k1 >> 4)) & 7][cl][k1 & 15], bwin[s + 1], h1);
+      for (int s = 0; s < 7 * MU / 4; s += 2) {
+        const T c0 = d0, c1 = d1;
+        if (s + 2 < 7 * MU / 4) {
+          d0 = dop(4 * s + 8 + kq);
+          d1 = dop(4 * s + 12 + kq);
+        }
+        if (s < 4 * nwin) {
+          h0 = Mfma<T>::run(c0, bwin[s], h0);
+          h1 = Mfma<T>::run(c1, bwin[s + 1], h1);
+        }
       }
     }
     // the band above last: its loads were issued last
@@ -935,20 +954,34 @@ __device__ inline void panel_gemm(const T* A, int64_t lda, const T* B, int64_t l
   for (int x = 0; x < TM; ++x)
 #pragma unroll
     for (int y = 0; y < TN; ++y) acc[x][y] = acc_t{0, 0, 0, 0};
+  // fp32: the fragments of k-step ks + 1 are read from LDS before the products of k-step ks
+  // are issued (two register sets, held in that order by a scheduling barrier), so that the
+  // reads' latency passes during the products, which take half as long as in fp64.  (In
+  // fp64 the compiler's own order was faster: 22 against 24 us per 256-deep task.)
   auto multiply = [&](int st) {
     const T* as = sm.buf + st * kStageElems;
     const T* bs = as + kSA * kKC;
+    T fa[2][TM], fb[2][TN];
+    auto frag = [&](int ks, int b) {
+#pragma unroll
+      for (int x = 0; x < TM; ++x) fa[b][x] = as[(4 * ks + kq) * kSA + wi0 + 16 * x + cl];
+#pragma unroll
+      for (int y = 0; y < TN; ++y) fb[b][y] = bs[(4 * ks + kq) * kSB + 16 * y + cl];
+    };
+    frag(0, 0);
 #pragma unroll
     for (int ks = 0; ks < kKC / 4; ++ks) {
-      T fa[TM], fb[TN];
-#pragma unroll
-      for (int x = 0; x < TM; ++x) fa[x] = as[(4 * ks + kq) * kSA + wi0 + 16 * x + cl];
-#pragma unroll
-      for (int y = 0; y < TN; ++y) fb[y] = bs[(4 * ks + kq) * kSB + 16 * y + cl];
+      const int b = sizeof(T) == 4 ? ks & 1 : 0;
+      if (sizeof(T) == 4) {
+        if (ks + 1 < kKC / 4) frag(ks + 1, b ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (ks > 0) {
+        frag(ks, 0);
+      }
 #pragma unroll
       for (int x = 0; x < TM; ++x)
 #pragma unroll
-        for (int y = 0; y < TN; ++y) acc[x][y] = Mfma<T>::run(fa[x], fb[y], acc[x][y]);
+        for (int y = 0; y < TN; ++y) acc[x][y] = Mfma<T>::run(fa[b][x], fb[b][y], acc[x][y]);
     }
   };
   if (kOld < 0) load_old();
