@@ -9,6 +9,11 @@
 //                     appears once, and that every tile of L and X ends final.  A queue
 //                     with that property drains with any number of resident workgroups:
 //                     the earliest unfinished task always has its waits met.
+//   run MB NB X B G WN WX WF S
+//                     executes the sweep's rules on an MB x NB grid with X XCDs of B band
+//                     workers (bands dealt in groups of G), WN / WX / WF near / next / far
+//                     update workers, for S seeded random schedules, and requires every
+//                     schedule to drain (sim_sweep).
 //   sweep MB NB       the band-update contributions of an MB x NB grid of 64 x 64 blocks:
 //                     per class, direction and target tile, the contributions that the
 //                     blocks publish must carry the ranks 0 .. expected - 1 exactly once,
@@ -169,6 +174,121 @@ static int check_sweep(int Mb, int Nb) {
   return 0;
 }
 
+// Executes the sweep's dependency rules with a given number of band workers per XCD and of
+// update workers per class, choosing among all enabled steps at random (seeded): a band
+// completes its next 64 x 64 block once the band above has completed that block and the
+// block's contribution counters of every class are complete, then publishes the block's
+// tasks (class queues, first in first out); an update worker claims the next task of its
+// class and applies it once every target counter equals the task's rank.  Fails if the run
+// reaches a state where work remains and no step is enabled.
+static int sim_sweep(int Mb, int Nb, int nx, int b, int gs, const int* W, int seeds) {
+  struct Task {
+    int dir, own, other, p0, p1;
+  };
+  char msg[512];
+  for (int seed = 1; seed <= seeds; ++seed) {
+    uint64_t rng = 0x9E3779B97F4A7C15ull * (uint64_t)seed + 12345;
+    auto rnd = [&](uint64_t k) {
+      rng = rng * 6364136223846793005ull + 1442695040888963407ull;
+      return (uint64_t)((rng >> 33) % k);
+    };
+    std::vector<int> progress(Mb, 0);
+    std::vector<std::vector<int>> xb(nx);  // bands of each XCD, in order
+    for (int K = 0; K < Mb; ++K) xb[(K / gs) % nx].push_back(K);
+    std::vector<size_t> xnext(nx, 0);
+    std::vector<int> slot((size_t)nx * b, -1);  // band held by each band worker
+    std::vector<int> cnt[2 * NCLS];             // vertical and horizontal counters per class
+    for (auto& c : cnt) c.assign((size_t)Mb * Nb, 0);
+    std::vector<Task> queue[NCLS];
+    std::vector<size_t> head(NCLS, 0);
+    std::vector<int> held[NCLS];
+    for (int c = 0; c < NCLS; ++c) held[c].assign(W[c], -1);
+    int64_t done_tasks = 0, steps = 0;
+    int bands_done = 0;
+    struct Act {
+      int kind, a, b;
+    };
+    std::vector<Act> acts;
+    for (;;) {
+      acts.clear();
+      for (int x = 0; x < nx; ++x)
+        for (int k = 0; k < b; ++k) {
+          const int K = slot[(size_t)x * b + k];
+          if (K < 0) {
+            if (xnext[x] < xb[x].size()) acts.push_back({0, x, k});  // claim a band
+            continue;
+          }
+          const int L = progress[K];
+          bool ok = K == 0 || progress[K - 1] > L;
+          for (int c = 0; c < NCLS && ok; ++c)
+            ok = cnt[2 * c][(size_t)K * Nb + L] >= expected_class(K, c) &&
+                 cnt[2 * c + 1][(size_t)K * Nb + L] >= expected_class(L, c);
+          if (ok) acts.push_back({1, x, k});  // complete the band's next block
+        }
+      for (int c = 0; c < NCLS; ++c)
+        for (int k = 0; k < W[c]; ++k) {
+          const int t = held[c][k];
+          if (t < 0) {
+            if (head[c] < queue[c].size()) acts.push_back({2, c, k});  // claim a task
+            continue;
+          }
+          const Task& q = queue[c][t];
+          bool ok = true;
+          for (int T = q.p0; T <= q.p1 && ok; ++T) {
+            const size_t idx = q.dir == 0 ? (size_t)T * Nb + q.other : (size_t)q.other * Nb + T;
+            ok = cnt[2 * c + q.dir][idx] == push_seq(T, q.own, c);
+          }
+          if (ok) acts.push_back({3, c, k});  // apply the task
+        }
+      if (acts.empty()) break;
+      const Act a = acts[rnd(acts.size())];
+      ++steps;
+      if (a.kind == 0) {
+        slot[(size_t)a.a * b + a.b] = xb[a.a][xnext[a.a]++];
+      } else if (a.kind == 1) {
+        const int K = slot[(size_t)a.a * b + a.b], L = progress[K]++;
+        int g0[6], g1[6], np[6];
+        block_groups(K, L, Mb, Nb, g0, g1, np);
+        for (int g = 0; g < 6; ++g) {
+          const int cls = g >> 1, dir = g & 1;
+          for (int k = 0; k < np[g]; ++k) {
+            const int p0 = g0[g] + kPanel * k;
+            const int p1 = p0 + kPanel - 1 < g1[g] ? p0 + kPanel - 1 : g1[g];
+            queue[cls].push_back({dir, dir == 0 ? K : L, dir == 0 ? L : K, p0, p1});
+          }
+        }
+        if (progress[K] == Nb) {
+          slot[(size_t)a.a * b + a.b] = -1;
+          ++bands_done;
+        }
+      } else if (a.kind == 2) {
+        held[a.a][a.b] = (int)head[a.a]++;
+      } else {
+        const Task& q = queue[a.a][held[a.a][a.b]];
+        for (int T = q.p0; T <= q.p1; ++T) {
+          const size_t idx = q.dir == 0 ? (size_t)T * Nb + q.other : (size_t)q.other * Nb + T;
+          cnt[2 * a.a + q.dir][idx] = push_seq(T, q.own, a.a) + 1;
+        }
+        held[a.a][a.b] = -1;
+        ++done_tasks;
+      }
+    }
+    int64_t queued = 0;
+    for (int c = 0; c < NCLS; ++c) queued += (int64_t)queue[c].size();
+    if (bands_done != Mb || done_tasks != queued) {
+      snprintf(msg, sizeof msg,
+               "sweep %dx%d, %d XCDs x %d band workers (groups of %d), update workers %d/%d/%d, "
+               "seed %d: stuck after %lld steps with %d of %d bands and %lld of %lld tasks done",
+               Mb, Nb, nx, b, gs, W[0], W[1], W[2], seed, (long long)steps, bands_done, Mb,
+               (long long)done_tasks, (long long)queued);
+      return fail(msg);
+    }
+  }
+  printf("sweep %dx%d, %d XCDs x %d band workers (groups of %d), update workers %d/%d/%d: "
+         "%d random schedules drained\n", Mb, Nb, nx, b, gs, W[0], W[1], W[2], seeds);
+  return 0;
+}
+
 int main(int argc, char** argv) {
   if (argc >= 3 && argv[1][0] == 'f') {
     std::vector<int> ns;
@@ -176,6 +296,13 @@ int main(int argc, char** argv) {
     return check_factor(ns);
   }
   if (argc == 4 && argv[1][0] == 's') return check_sweep(atoi(argv[2]), atoi(argv[3]));
-  fprintf(stderr, "usage: %s factor P0 [P1] | sweep MB NB\n", argv[0]);
+  if (argc == 11 && argv[1][0] == 'r') {
+    const int W[3] = {atoi(argv[7]), atoi(argv[8]), atoi(argv[9])};
+    return sim_sweep(atoi(argv[2]), atoi(argv[3]), atoi(argv[4]), atoi(argv[5]), atoi(argv[6]),
+                     W, atoi(argv[10]));
+  }
+  fprintf(stderr,
+          "usage: %s factor P0 [P1] | sweep MB NB | run MB NB XCDS BANDWORKERS GROUP NEAR NEXT "
+          "FAR SEEDS\n", argv[0]);
   return 2;
 }

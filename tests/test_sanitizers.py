@@ -43,7 +43,8 @@ def test_schedule_checker_clean(tmp_path):
          ["-I", CSRC, os.path.join(ROOT, "tests", "native", "schedule_check.cpp"), "-o", exe])
     for args in (["factor", "64", "64"], ["factor", "224", "64"], ["factor", "10", "17"],
                  ["factor", "2", "3"], ["factor", "1", "1"], ["sweep", "64", "64"],
-                 ["sweep", "224", "64"], ["sweep", "5", "9"], ["sweep", "1", "1"]):
+                 ["sweep", "224", "64"], ["sweep", "5", "9"], ["sweep", "1", "1"],
+                 ["run", "21", "6", "3", "2", "1", "1", "2", "1", "2"]):
         _run([exe] + args, env=ENV_NO_LEAKS)
 
 

@@ -6,8 +6,10 @@ queue in order and requires every wait of every task to be met by the tasks befo
 (then the queue drains with any number of resident workgroups: the earliest unfinished
 task can always run); for the sweep it requires the band-update contributions each target
 tile waits for to be published exactly once, with ranks in the order of their sources (so
-every class queue, served first-in first-out, only waits for earlier tasks).  Shapes: the
-five layers (in 64-wide tiles), the odd sizes of the parity tests and a few extremes.
+every class queue, served first-in first-out, only waits for earlier tasks), and it executes
+the sweep's rules with fixed numbers of band and update workers under random schedules,
+which must all drain.  Shapes: the five layers (in 64-wide tiles), the odd sizes of the
+parity tests and a few extremes.
 """
 import os
 import shutil
@@ -51,3 +53,28 @@ def test_factor_queue_never_waits_for_a_later_task(checker, tiles):
 def test_sweep_contributions_complete_and_in_source_order(checker, blocks):
     out = _run(checker, "sweep", *blocks)
     assert "ranks complete" in out
+
+
+# (blocks, XCDs, band workers per XCD, bands per group, near / next / far update workers):
+# the five layers with the plans the sweep uses (eight XCDs; nine band workers in groups of
+# eight bands for the 4096-wide layer, four in groups of four for the larger ones) and with
+# the fewest workers the kernel allows (one per role), plus odd grids and XCD counts
+SIM_CASES = [
+    ((1, 1), 8, 1, 1, (1, 1, 1)), ((8, 8), 8, 3, 1, (4, 2, 17)),
+    ((64, 64), 8, 9, 8, (32, 16, 136)), ((64, 64), 1, 1, 1, (1, 1, 1)),
+    ((64, 64), 8, 1, 1, (1, 1, 1)), ((224, 64), 8, 4, 4, (40, 24, 160)),
+    ((64, 224), 8, 4, 4, (40, 24, 160)), ((128, 128), 8, 4, 4, (40, 24, 160)),
+    ((224, 64), 1, 1, 1, (1, 1, 1)), ((5, 9), 2, 1, 4, (1, 1, 1)), ((21, 6), 3, 2, 1, (1, 2, 1)),
+    ((3, 40), 4, 2, 2, (2, 1, 3)), ((256, 16), 8, 4, 4, (40, 24, 160)),
+]
+
+
+@pytest.mark.parametrize("case", SIM_CASES, ids=lambda c: "x".join(map(str, c[0])) +
+                         f"-{c[1]}xcd-{c[2]}bw-g{c[3]}-w" + "_".join(map(str, c[4])))
+def test_sweep_drains_under_random_schedules(checker, case):
+    # the rules executed with a fixed number of band and update workers, every enabled step
+    # chosen at random: every schedule must finish (no worker set can wait on a task that
+    # only a blocked worker could run)
+    (mb, nb), nx, bw, gs, (wn, wx, wf) = case
+    out = _run(checker, "run", mb, nb, nx, bw, gs, wn, wx, wf, 3)
+    assert "random schedules drained" in out
