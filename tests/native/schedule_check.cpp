@@ -9,6 +9,8 @@
 //                     appears once, and that every tile of L and X ends final.  A queue
 //                     with that property drains with any number of resident workgroups:
 //                     the earliest unfinished task always has its waits met.
+//   qrun P0 [P1] W S  executes the factor's queue with W workgroups for S seeded random
+//                     schedules and requires every schedule to drain (sim_factor).
 //   run MB NB X B G WN WX WF S
 //                     executes the sweep's rules on an MB x NB grid with X XCDs of B band
 //                     workers (bands dealt in groups of G), WN / WX / WF near / next / far
@@ -174,6 +176,76 @@ static int check_sweep(int Mb, int Nb) {
   return 0;
 }
 
+// Executes the factor's queue with W workgroups: a free one claims the next task in queue
+// order, a claimed task runs once every counter it waits for has its value, and each step is
+// chosen at random among the enabled ones (seeded).  Fails if work remains and nothing can
+// run.
+static int sim_factor(const std::vector<int>& ns, int W, int seeds) {
+  struct T {
+    int q;
+    CholTask t;
+  };
+  std::vector<T> order;
+  int maxn = 0;
+  for (int n : ns) maxn = n > maxn ? n : maxn;
+  for (int g = 0; g < maxn; ++g)
+    for (int q = 0; q < (int)ns.size(); ++q) {
+      if (g >= ns[q]) continue;
+      const int64_t gsz = group_size(ns[q], g);
+      for (int64_t r = 0; r < gsz; ++r) order.push_back({q, chol_decode(ns[q], g, r)});
+    }
+  char msg[256];
+  for (int seed = 1; seed <= seeds; ++seed) {
+    uint64_t rng = 0x2545F4914F6CDD1Dull * (uint64_t)seed + 99;
+    auto rnd = [&](uint64_t k) {
+      rng = rng * 6364136223846793005ull + 1442695040888963407ull;
+      return (uint64_t)((rng >> 33) % k);
+    };
+    std::vector<std::vector<int>> cnt[2];
+    for (int q = 0; q < (int)ns.size(); ++q)
+      cnt[q].assign(2, std::vector<int>((size_t)ns[q] * ns[q], 0));
+    std::vector<int64_t> held(W, -1);
+    size_t next = 0;
+    int64_t done = 0;
+    std::vector<std::pair<int, int>> acts;
+    for (;;) {
+      acts.clear();
+      for (int k = 0; k < W; ++k) {
+        if (held[k] < 0) {
+          if (next < order.size()) acts.push_back({0, k});
+          continue;
+        }
+        const T& e = order[held[k]];
+        CholWait w[4];
+        const int nw = chol_waits(ns[e.q], e.t, w);
+        bool ok = true;
+        for (int c = 0; c < nw && ok; ++c) ok = cnt[e.q][w[c].arr][w[c].idx] >= w[c].val;
+        if (ok) acts.push_back({1, k});
+      }
+      if (acts.empty()) break;
+      const auto a = acts[rnd(acts.size())];
+      if (a.first == 0) {
+        held[a.second] = (int64_t)next++;
+      } else {
+        const T& e = order[held[a.second]];
+        const CholWait sg = chol_signal(ns[e.q], e.t);
+        cnt[e.q][sg.arr][sg.idx] = sg.val;
+        held[a.second] = -1;
+        ++done;
+      }
+    }
+    if (done != (int64_t)order.size()) {
+      snprintf(msg, sizeof msg, "factor with %d workgroups, seed %d: stuck with %lld of %lld tasks done",
+               W, seed, (long long)done, (long long)order.size());
+      return fail(msg);
+    }
+  }
+  printf("factor");
+  for (int n : ns) printf(" %d", n);
+  printf(" with %d workgroups: %d random schedules drained\n", W, seeds);
+  return 0;
+}
+
 // Executes the sweep's dependency rules with a given number of band workers per XCD and of
 // update workers per class, choosing among all enabled steps at random (seeded): a band
 // completes its next 64 x 64 block once the band above has completed that block and the
@@ -296,13 +368,18 @@ int main(int argc, char** argv) {
     return check_factor(ns);
   }
   if (argc == 4 && argv[1][0] == 's') return check_sweep(atoi(argv[2]), atoi(argv[3]));
+  if ((argc == 5 || argc == 6) && argv[1][0] == 'q') {  // qrun P0 [P1] W SEEDS
+    std::vector<int> ns;
+    for (int k = 2; k < argc - 2; ++k) ns.push_back(atoi(argv[k]));
+    return sim_factor(ns, atoi(argv[argc - 2]), atoi(argv[argc - 1]));
+  }
   if (argc == 11 && argv[1][0] == 'r') {
     const int W[3] = {atoi(argv[7]), atoi(argv[8]), atoi(argv[9])};
     return sim_sweep(atoi(argv[2]), atoi(argv[3]), atoi(argv[4]), atoi(argv[5]), atoi(argv[6]),
                      W, atoi(argv[10]));
   }
   fprintf(stderr,
-          "usage: %s factor P0 [P1] | sweep MB NB | run MB NB XCDS BANDWORKERS GROUP NEAR NEXT "
-          "FAR SEEDS\n", argv[0]);
+          "usage: %s factor P0 [P1] | qrun P0 [P1] WORKGROUPS SEEDS | sweep MB NB | run MB NB "
+          "XCDS BANDWORKERS GROUP NEAR NEXT FAR SEEDS\n", argv[0]);
   return 2;
 }

@@ -78,3 +78,14 @@ def test_sweep_drains_under_random_schedules(checker, case):
     (mb, nb), nx, bw, gs, (wn, wx, wf) = case
     out = _run(checker, "run", mb, nb, nx, bw, gs, wn, wx, wf, 3)
     assert "random schedules drained" in out
+
+
+@pytest.mark.parametrize("case", [((64, 64), 1), ((64, 64), 7), ((64, 64), 512), ((224, 64), 3),
+                                  ((224, 64), 64), ((128,), 5), ((10, 17), 2), ((1, 1), 1)],
+                         ids=lambda c: "x".join(map(str, c[0])) + f"-{c[1]}wg")
+def test_factor_queue_drains_under_random_schedules(checker, case):
+    # the factor's queue executed by a fixed number of workgroups (claims in queue order,
+    # a task runs once its counters are met), enabled steps chosen at random
+    tiles, wg = case
+    out = _run(checker, "qrun", *tiles, wg, 2)
+    assert "random schedules drained" in out
